@@ -1,0 +1,53 @@
+"""The pins are strong enough: each plausible mistake planted in a copy of the
+oracle's C source (on the CPU, in a temporary directory) makes at least one
+pin fail. The real oracle file is never modified."""
+import os
+
+import pytest
+
+import oracle as O
+from oracle_pins import PINS
+
+SRC = os.path.join(os.path.dirname(O.__file__), "gqa_oracle.c")
+
+# (name, exact text in the oracle, replacement)
+MUTANTS = [
+    ("group_floor_plus_one", "int64_t g1 = (num + H - 1) / H;", "int64_t g1 = num / H + 1;"),
+    ("group_off_by_one", "return (int)(g1 - 1);", "return (int)(g1 % G);"),
+    ("dropped_scale", "s[t] = scale * dot;", "s[t] = dot;"),
+    ("exp_sign", "s[t] = exp(s[t] - m);", "s[t] = exp(m - s[t]);"),
+    ("no_normalise", "out[d] = acc / denom;", "out[d] = acc;"),
+    ("keys_from_values", "dot += widen(q, q_off + d, dtype) * widen(k,", "dot += widen(q, q_off + d, dtype) * widen(v,"),
+    ("head_major_cache", "int64_t key_stride = (int64_t)G * D; ", "int64_t key_stride = (int64_t)D; "),
+    ("causal_drops_diagonal", "int L = causal ? t + 1 : T;", "int L = causal ? t : T;"),
+    ("causal_ignored", "int L = causal ? t + 1 : T;", "int L = T;"),
+    ("prefill_scale_dh", "double scale = 1.0 / sqrt((double)D);", "double scale = 1.0 / (double)D;"),
+    ("pool_divides_by_H", "o[d] = o[d] / (double)members;", "o[d] = o[d] / (double)H;"),
+    ("cache_single_tensor", "return 2.0 * (double)kv_heads", "return 1.0 * (double)kv_heads"),
+    ("clamp_off_by_one", "if (L > Tmax)\n        return Tmax;", "if (L > Tmax)\n        return Tmax - 1;"),
+    ("bf16_low_half", "<< 16;\n        float f;", ";\n        float f;"),
+    ("prefill_wrong_group", "int g = oracle_group_of_head(h, H, G);\n        int L = causal",
+     "int g = h % G;\n        int L = causal"),
+]
+
+
+def _run_pins(lib):
+    failed = []
+    for pin in PINS:
+        try:
+            pin(lib)
+        except Exception as e:  # any assertion or crash-free error counts as caught
+            failed.append((pin.__name__, type(e).__name__))
+    return failed
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    src = tmp_path / f"{name}.c"
+    src.write_text(text.replace(old, new))
+    so = O.build(str(src), str(tmp_path / f"{name}.so"))
+    lib = O.load(so)
+    failed = _run_pins(lib)
+    assert failed, f"planted mistake {name} passed every pin"
