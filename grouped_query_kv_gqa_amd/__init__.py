@@ -1,0 +1,170 @@
+"""grouped_query_kv_gqa_amd -- grouped-query attention over a KV cache on
+AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libgqa.so`` (C ABI in ``include/gqa.h``). Every
+step of the computation runs in the library's HIP kernels; this module only
+checks torch tensors (device, dtype, shape, contiguity), passes their data
+pointers and the current HIP stream, and raises ``GqaError`` on a non-zero
+status. There is no CPU fallback: if the library is missing, every call
+raises.
+
+  decode(q, k_cache, v_cache, seqlens, scale=None, out=None, split_tokens=0)
+  prefill(q, k, v, causal=True, out=None)
+  mean_pool_kv(x, G, out=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["GqaError", "decode", "prefill", "mean_pool_kv", "decode_plan", "library_path", "load_library"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libgqa.so")
+
+GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_HIP = 0, 1, 2, 3
+GQA_BF16, GQA_FP32 = 0, 1
+
+_lib = None
+
+
+class GqaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"gqa status {status}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libgqa.so (torch is imported first, so the library binds to the
+    HIP runtime torch already loaded)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run `python -m grouped_query_kv_gqa_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    lib.gqa_decode.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp]
+    lib.gqa_decode_ex.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, i32]
+    lib.gqa_prefill.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
+    lib.gqa_mean_pool_kv.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp]
+    lib.gqa_decode_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32),
+                                    ctypes.POINTER(i32), ctypes.POINTER(i64)]
+    for fn in ("gqa_decode", "gqa_decode_ex", "gqa_prefill", "gqa_mean_pool_kv", "gqa_decode_plan"):
+        getattr(lib, fn).restype = i32
+    lib.gqa_status_string.argtypes = [i32]
+    lib.gqa_status_string.restype = ctypes.c_char_p
+    lib.gqa_last_error.argtypes = []
+    lib.gqa_last_error.restype = ctypes.c_char_p
+    lib.gqa_abi_version.argtypes = []
+    lib.gqa_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != GQA_OK:
+        lib = load_library()
+        raise GqaError(status, lib.gqa_last_error().decode() or lib.gqa_status_string(status).decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GQA_BF16
+    if t.dtype == torch.float32:
+        return GQA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _need_device(*ts: torch.Tensor):
+    dev = ts[0].device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    for t in ts:
+        if t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return dev
+
+
+def _stream_ptr(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def decode(q, k_cache, v_cache, seqlens, scale: float | None = None, out=None, split_tokens: int = 0):
+    """One decode step. q [B,H,D]; k_cache, v_cache [B,Tmax,G,D]; seqlens [B]
+    int32 on the device. Returns out [B,H,D] (same dtype as q)."""
+    lib = load_library()
+    B, H, D = q.shape
+    Bk, Tmax, G, Dk = k_cache.shape
+    if (Bk, Dk) != (B, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch between q, k_cache and v_cache")
+    if seqlens.dtype != torch.int32 or tuple(seqlens.shape) != (B,):
+        raise ValueError("seqlens must be int32 of shape [B]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share a dtype")
+    dev = _need_device(q, k_cache, v_cache, seqlens)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_device(out)
+        if out.shape != q.shape or out.dtype != q.dtype or out.device != dev:
+            raise ValueError("out must match q")
+    if scale is None:
+        scale = D ** -0.5
+    with torch.cuda.device(dev):
+        _check(lib.gqa_decode_ex(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr(),
+                                 B, H, G, D, Tmax, float(scale), _dtype_code(q), out.data_ptr(),
+                                 _stream_ptr(dev), int(split_tokens)))
+    return out
+
+
+def prefill(q, k, v, causal: bool = True, out=None):
+    """q [B,T,H,D]; k, v [B,T,G,D]. Returns out [B,T,H,D], scale 1/sqrt(D)."""
+    lib = load_library()
+    B, T, H, D = q.shape
+    if k.shape[:2] != (B, T) or k.shape[3] != D or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch between q, k and v")
+    G = k.shape[2]
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    dev = _need_device(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != dev or not out.is_contiguous():
+        raise ValueError("out must match q")
+    with torch.cuda.device(dev):
+        _check(lib.gqa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, H, G, D, int(bool(causal)),
+                               _dtype_code(q), out.data_ptr(), _stream_ptr(dev)))
+    return out
+
+
+def mean_pool_kv(x, G: int, out=None):
+    """x [N,H,D] -> [N,G,D]: each group is the mean of its H/G heads."""
+    lib = load_library()
+    N, H, D = x.shape
+    dev = _need_device(x)
+    if out is None:
+        out = torch.empty((N, G, D), dtype=x.dtype, device=dev)
+    elif tuple(out.shape) != (N, G, D) or out.dtype != x.dtype or out.device != dev or not out.is_contiguous():
+        raise ValueError("out must be [N,G,D] like x")
+    with torch.cuda.device(dev):
+        _check(lib.gqa_mean_pool_kv(x.data_ptr(), N, H, G, D, _dtype_code(x), out.data_ptr(), _stream_ptr(dev)))
+    return out
+
+
+def decode_plan(B, H, G, D, Tmax, dtype=torch.bfloat16, split_tokens=0, cu_count=256):
+    """(chunk_tokens, num_splits, workspace_bytes) of the decode split plan; host only."""
+    lib = load_library()
+    chunk, splits, ws = ctypes.c_int(), ctypes.c_int(), ctypes.c_int64()
+    code = GQA_BF16 if dtype == torch.bfloat16 else GQA_FP32
+    _check(lib.gqa_decode_plan(B, H, G, D, Tmax, code, split_tokens, cu_count, ctypes.byref(chunk),
+                               ctypes.byref(splits), ctypes.byref(ws)))
+    return chunk.value, splits.value, ws.value

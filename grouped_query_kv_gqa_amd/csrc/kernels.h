@@ -1,0 +1,39 @@
+// kernels.h -- launchers of the libgqa HIP kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "plan.h"
+
+namespace gqa {
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const int32_t *seqlens;
+    int B, H, G, D, Tmax;
+    float scale;
+    void *out;
+    float *part;    // split partial rows, or null when the plan has one split
+    float *lse;     // split log-sum-exp values (base 2)
+    int *counters;  // per (sequence, group, head tile) arrival counters, zero between launches
+    hipStream_t stream;
+};
+
+hipError_t launch_decode(const DecodePlan &plan, const DecodeArgs &args, gqa_dtype dtype);
+
+struct PrefillArgs {
+    const void *q, *k, *v;
+    int B, T, H, G, D;
+    int causal;
+    void *out;
+    hipStream_t stream;
+};
+
+hipError_t launch_prefill(const PrefillArgs &args, gqa_dtype dtype);
+
+hipError_t launch_mean_pool(const void *in, int64_t N, int H, int G, int D, gqa_dtype dtype, void *out,
+                            hipStream_t stream);
+
+hipError_t launch_fill_i32(int *p, int64_t n, int value, hipStream_t stream);
+
+}  // namespace gqa

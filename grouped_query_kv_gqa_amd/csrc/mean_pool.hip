@@ -1,0 +1,131 @@
+// mean_pool.hip -- averaging conversion of multi-head key/value heads into G
+// groups, and a small fill kernel used by the host library.
+//
+// out[n,g,:] = (1/r) * sum_{j<r} in[n, g*r + j, :] with r = H/G: each new
+// group starts as the mean of the original heads assigned to it
+// ("Grouped-Query Attention" (llm-arch-kb), section 2 Derivation, Uptraining
+// recipe; crackai.dev paper card, How It Works).
+//
+// HBM-bound: every thread owns 8 consecutive d of one (n, g) output, reads the
+// group's r input heads with 16-byte (bf16) or 32-byte (fp32) loads, sums in
+// fp32 in head order and divides once by r, so G = H copies exactly.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace gqa {
+
+namespace {
+
+template <typename T>
+struct Chunk8;
+
+template <>
+struct Chunk8<__bf16> {
+    static __device__ __forceinline__ void load(const __bf16 *p, float (&x)[8])
+    {
+        const u32x4_t u = *reinterpret_cast<const u32x4_t *>(p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = bf16_bits_to_f32(u[j] & 0xffffu);
+            x[2 * j + 1] = bf16_bits_to_f32(u[j] >> 16);
+        }
+    }
+    static __device__ __forceinline__ void store(__bf16 *p, const float (&x)[8])
+    {
+        u32x4_t u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            u[j] = pack_bf16x2(x[2 * j], x[2 * j + 1]);
+        *reinterpret_cast<u32x4_t *>(p) = u;
+    }
+};
+
+template <>
+struct Chunk8<float> {
+    static __device__ __forceinline__ void load(const float *p, float (&x)[8])
+    {
+        const f32x4_t a = reinterpret_cast<const f32x4_t *>(p)[0];
+        const f32x4_t b = reinterpret_cast<const f32x4_t *>(p)[1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[j] = a[j];
+            x[4 + j] = b[j];
+        }
+    }
+    static __device__ __forceinline__ void store(float *p, const float (&x)[8])
+    {
+        reinterpret_cast<f32x4_t *>(p)[0] = (f32x4_t){x[0], x[1], x[2], x[3]};
+        reinterpret_cast<f32x4_t *>(p)[1] = (f32x4_t){x[4], x[5], x[6], x[7]};
+    }
+};
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+mean_pool_kernel(const T *__restrict__ in, int64_t N, int H, int G, int D, T *__restrict__ out)
+{
+    const int r = H / G;
+    const int chunks = D / 8;
+    const int64_t total = N * G * chunks;
+    const float rf = (float)r;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int c = (int)(i % chunks);
+        const int64_t ng = i / chunks;  // n * G + g
+        const int g = (int)(ng % G);
+        const int64_t n = ng / G;
+        const T *src = in + (n * H + (int64_t)g * r) * D + c * 8;
+        float acc[8], x[8];
+        Chunk8<T>::load(src, acc);
+        for (int j = 1; j < r; ++j) {
+            Chunk8<T>::load(src + (int64_t)j * D, x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                acc[e] += x[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[e] = acc[e] / rf;
+        Chunk8<T>::store(out + ng * D + c * 8, acc);
+    }
+}
+
+__global__ void fill_i32_kernel(int *p, int64_t n, int value)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = value;
+}
+
+unsigned grid_for(int64_t items, int block)
+{
+    int64_t g = (items + block - 1) / block;
+    const int64_t cap = 256 * 32;  // enough resident waves to stream HBM
+    if (g > cap)
+        g = cap;
+    return (unsigned)(g < 1 ? 1 : g);
+}
+
+}  // namespace
+
+hipError_t launch_mean_pool(const void *in, int64_t N, int H, int G, int D, gqa_dtype dtype, void *out,
+                            hipStream_t stream)
+{
+    const int64_t items = N * G * (D / 8);
+    const unsigned grid = grid_for(items, 256);
+    if (dtype == GQA_FP32)
+        mean_pool_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float *>(in), N, H, G, D,
+                                                          static_cast<float *>(out));
+    else
+        mean_pool_kernel<__bf16><<<grid, 256, 0, stream>>>(static_cast<const __bf16 *>(in), N, H, G, D,
+                                                           static_cast<__bf16 *>(out));
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int *p, int64_t n, int value, hipStream_t stream)
+{
+    if (n <= 0)
+        return hipSuccess;
+    fill_i32_kernel<<<grid_for(n, 256), 256, 0, stream>>>(p, n, value);
+    return hipGetLastError();
+}
+
+}  // namespace gqa

@@ -1,0 +1,194 @@
+// plan.cpp -- host-side argument checks and launch planning for libgqa.
+// Pure C++ (no HIP); see plan.h.
+#include "plan.h"
+
+#include <cmath>
+
+namespace gqa {
+
+namespace {
+
+gqa_status fail(std::string *err, gqa_status s, const std::string &msg)
+{
+    if (err)
+        *err = msg;
+    return s;
+}
+
+bool aligned16(const void *p)
+{
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+int64_t ceil_div(int64_t a, int64_t b)
+{
+    return (a + b - 1) / b;
+}
+
+int64_t round_up(int64_t a, int64_t m)
+{
+    return ceil_div(a, m) * m;
+}
+
+bool dtype_ok(gqa_dtype dt)
+{
+    return dt == GQA_BF16 || dt == GQA_FP32;
+}
+
+}  // namespace
+
+int64_t elem_size(gqa_dtype dt)
+{
+    return dt == GQA_FP32 ? 4 : 2;
+}
+
+bool ranges_overlap(const void *a, int64_t a_bytes, const void *b, int64_t b_bytes)
+{
+    if (!a || !b || a_bytes <= 0 || b_bytes <= 0)
+        return false;
+    uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + static_cast<uintptr_t>(b_bytes) && b0 < a0 + static_cast<uintptr_t>(a_bytes);
+}
+
+gqa_status check_decode(const void *q, const void *k, const void *v, const int32_t *seqlens, int B, int H,
+                        int G, int d_h, int Tmax, float scale, gqa_dtype dtype, const void *out,
+                        std::string *err)
+{
+    if (B < 0 || Tmax < 0)
+        return fail(err, GQA_ERR_INVALID_ARG, "B and Tmax must be >= 0");
+    if (H < 1 || G < 1 || d_h < 1)
+        return fail(err, GQA_ERR_INVALID_ARG, "H, G and d_h must be >= 1");
+    if (H % G != 0)
+        return fail(err, GQA_ERR_INVALID_ARG, "G must divide H");
+    if (!dtype_ok(dtype))
+        return fail(err, GQA_ERR_UNSUPPORTED, "unknown dtype");
+    if (d_h != 64 && d_h != 128)
+        return fail(err, GQA_ERR_UNSUPPORTED, "d_h must be 64 or 128");
+    if (!std::isfinite(scale))
+        return fail(err, GQA_ERR_INVALID_ARG, "scale must be finite");
+    if (B == 0)
+        return GQA_OK;
+    if (!q || !seqlens || !out || (Tmax > 0 && (!k || !v)))
+        return fail(err, GQA_ERR_INVALID_ARG, "null pointer");
+    if (!aligned16(q) || !aligned16(out) || (Tmax > 0 && (!aligned16(k) || !aligned16(v))))
+        return fail(err, GQA_ERR_INVALID_ARG, "q, k_cache, v_cache and out must be 16-byte aligned");
+    const int64_t e = elem_size(dtype);
+    const int64_t q_bytes = (int64_t)B * H * d_h * e;
+    const int64_t kv_bytes = (int64_t)B * Tmax * G * d_h * e;
+    if (ranges_overlap(out, q_bytes, q, q_bytes) || ranges_overlap(out, q_bytes, k, kv_bytes) ||
+        ranges_overlap(out, q_bytes, v, kv_bytes) || ranges_overlap(out, q_bytes, seqlens, 4 * (int64_t)B))
+        return fail(err, GQA_ERR_INVALID_ARG, "out overlaps an input");
+    return GQA_OK;
+}
+
+gqa_status plan_decode(int B, int H, int G, int d_h, int Tmax, gqa_dtype dtype, int split_tokens,
+                       int cu_count, DecodePlan *plan, std::string *err)
+{
+    if (B < 0 || Tmax < 0 || H < 1 || G < 1 || d_h < 1)
+        return fail(err, GQA_ERR_INVALID_ARG, "bad sizes");
+    if (H % G != 0)
+        return fail(err, GQA_ERR_INVALID_ARG, "G must divide H");
+    if (!dtype_ok(dtype))
+        return fail(err, GQA_ERR_UNSUPPORTED, "unknown dtype");
+    if (d_h != 64 && d_h != 128)
+        return fail(err, GQA_ERR_UNSUPPORTED, "d_h must be 64 or 128");
+    if (split_tokens < 0)
+        return fail(err, GQA_ERR_INVALID_ARG, "split_tokens must be >= 0");
+    DecodePlan p;
+    p.r = H / G;
+    p.nt = p.r <= 16 ? 1 : (p.r <= 32 ? 2 : 4);
+    p.head_tiles = (int)ceil_div(p.r, 16 * p.nt);
+    if (dtype == GQA_FP32 || Tmax == 0 || B == 0) {
+        p.chunk = (int)round_up(Tmax > 0 ? Tmax : 1, kDecodeTile);
+        p.splits = 1;
+    } else {
+        int64_t chunk;
+        if (split_tokens > 0) {
+            chunk = round_up(split_tokens, kDecodeTile);
+        } else {
+            const int64_t cus = cu_count > 0 ? cu_count : 256;
+            const int64_t pairs = (int64_t)B * G * p.head_tiles;
+            const int64_t want = ceil_div(4 * cus, pairs);  // workgroups per (sequence, head tile)
+            chunk = round_up(ceil_div(Tmax, want), kDecodeTile);
+            if (chunk < kMinAutoChunk)
+                chunk = kMinAutoChunk;
+        }
+        if (chunk > round_up(Tmax, kDecodeTile))
+            chunk = round_up(Tmax, kDecodeTile);
+        p.chunk = (int)chunk;
+        p.splits = (int)ceil_div(Tmax, chunk);
+    }
+    if (p.splits > 1) {
+        const int64_t rows = (int64_t)B * H;
+        // counters first, then partial rows, then log-sum-exp values
+        int64_t off = 0;
+        p.counter_offset = off;
+        p.n_counters = (int64_t)B * G * p.head_tiles;
+        off = round_up(off + p.n_counters * 4, 256);
+        p.part_offset = off;
+        off = round_up(off + rows * p.splits * d_h * 4, 256);
+        p.lse_offset = off;
+        off = round_up(off + rows * p.splits * 4, 256);
+        p.workspace_bytes = off;
+    }
+    if (plan)
+        *plan = p;
+    return GQA_OK;
+}
+
+gqa_status check_prefill(const void *q, const void *k, const void *v, int B, int T, int H, int G, int d_h,
+                         int causal, gqa_dtype dtype, const void *out, std::string *err)
+{
+    if (B < 0 || T < 0)
+        return fail(err, GQA_ERR_INVALID_ARG, "B and T must be >= 0");
+    if (H < 1 || G < 1 || d_h < 1)
+        return fail(err, GQA_ERR_INVALID_ARG, "H, G and d_h must be >= 1");
+    if (H % G != 0)
+        return fail(err, GQA_ERR_INVALID_ARG, "G must divide H");
+    if (causal != 0 && causal != 1)
+        return fail(err, GQA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (!dtype_ok(dtype))
+        return fail(err, GQA_ERR_UNSUPPORTED, "unknown dtype");
+    if (d_h != 64 && d_h != 128)
+        return fail(err, GQA_ERR_UNSUPPORTED, "d_h must be 64 or 128");
+    if (B == 0 || T == 0)
+        return GQA_OK;
+    if (!q || !k || !v || !out)
+        return fail(err, GQA_ERR_INVALID_ARG, "null pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(err, GQA_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+    const int64_t e = elem_size(dtype);
+    const int64_t q_bytes = (int64_t)B * T * H * d_h * e;
+    const int64_t kv_bytes = (int64_t)B * T * G * d_h * e;
+    if (ranges_overlap(out, q_bytes, q, q_bytes) || ranges_overlap(out, q_bytes, k, kv_bytes) ||
+        ranges_overlap(out, q_bytes, v, kv_bytes))
+        return fail(err, GQA_ERR_INVALID_ARG, "out overlaps an input");
+    return GQA_OK;
+}
+
+gqa_status check_mean_pool(const void *in, int64_t N, int H, int G, int d_h, gqa_dtype dtype,
+                           const void *out, std::string *err)
+{
+    if (N < 0)
+        return fail(err, GQA_ERR_INVALID_ARG, "N must be >= 0");
+    if (H < 1 || G < 1 || d_h < 1)
+        return fail(err, GQA_ERR_INVALID_ARG, "H, G and d_h must be >= 1");
+    if (H % G != 0)
+        return fail(err, GQA_ERR_INVALID_ARG, "G must divide H");
+    if (!dtype_ok(dtype))
+        return fail(err, GQA_ERR_UNSUPPORTED, "unknown dtype");
+    if (d_h % 8 != 0)
+        return fail(err, GQA_ERR_UNSUPPORTED, "d_h must be a multiple of 8");
+    if (N == 0)
+        return GQA_OK;
+    if (!in || !out)
+        return fail(err, GQA_ERR_INVALID_ARG, "null pointer");
+    if (!aligned16(in) || !aligned16(out))
+        return fail(err, GQA_ERR_INVALID_ARG, "in and out must be 16-byte aligned");
+    const int64_t e = elem_size(dtype);
+    if (ranges_overlap(out, N * G * d_h * e, in, N * H * d_h * e))
+        return fail(err, GQA_ERR_INVALID_ARG, "out overlaps in");
+    return GQA_OK;
+}
+
+}  // namespace gqa

@@ -1,0 +1,157 @@
+/*
+ * gqa.h -- C ABI of libgqa.so: grouped-query attention (GQA) forward over a
+ * key/value cache on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (sources are web pages; each call below names its passage):
+ *   H query heads are split into G contiguous groups of r = H/G heads; query
+ *   head h (0-indexed) reads key/value head g(h) = floor(h*G/H) = h / r, which
+ *   is the 1-indexed rule g(i) = ceil(i*G/H) of "Grouped-Query Attention"
+ *   (llm-arch-kb), section 2 Derivation, The grouping. Each head then does
+ *   ordinary scaled dot-product attention against its group's keys and values
+ *   (same page, section 3 Reference implementation: scores divided by
+ *   sqrt(d_h), causal mask, softmax over keys, times v). G = H is multi-head
+ *   attention and G = 1 is multi-query attention (same page, section 1
+ *   Premise; crackai.dev paper card, How It Works).
+ *
+ * Conventions shared by every call:
+ *   - Tensors are dense, row-major, caller-owned DEVICE memory with the head
+ *     dimension d_h innermost and contiguous. The library keeps no pointer
+ *     after a call returns and never frees caller memory.
+ *   - One dtype for all floating-point tensors of a call: GQA_BF16 (bf16
+ *     storage, fp32 accumulation and softmax, bf16 output rounded to nearest
+ *     even) or GQA_FP32 (fp32 storage and arithmetic; a debug path).
+ *   - Calls are asynchronous on `stream` (0 = the null stream): they return
+ *     once the work is queued. Work on one stream runs in order.
+ *   - All argument checks run on the host before anything is queued. A
+ *     failing check returns a status and queues nothing. `out` must not
+ *     overlap any input. q, k, v and out must be 16-byte aligned.
+ *   - A batch of zero sequences (B = 0, or N = 0 for pooling) is valid and
+ *     queues nothing; its pointers may be NULL.
+ *   - GQA_ERR_HIP means the HIP runtime reported an error while queueing;
+ *     gqa_last_error() then holds its text.
+ *   - Thread safety: calls may be made from several host threads. Calls that
+ *     share a stream are serialised by that stream.
+ */
+#ifndef GQA_H_
+#define GQA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t; /* same type as HIP's own typedef */
+
+typedef enum gqa_status {
+    GQA_OK = 0,
+    GQA_ERR_INVALID_ARG = 1, /* null pointer, negative size, G not dividing H, misalignment, aliasing */
+    GQA_ERR_UNSUPPORTED = 2, /* valid but not built: d_h other than 64 or 128, unknown dtype */
+    GQA_ERR_HIP = 3          /* the HIP runtime failed; see gqa_last_error() */
+} gqa_status;
+
+typedef enum gqa_dtype { GQA_BF16 = 0, GQA_FP32 = 1 } gqa_dtype;
+
+/*
+ * gqa_decode -- one decode step: one new query per sequence against that
+ * sequence's whole cache.
+ * Defines: "Grouped-Query Attention" (llm-arch-kb), section 1 Premise (at a
+ * decode step every cached key and value is read to produce one token) and
+ * section 2 Derivation (head i attends over its cached keys and values; The
+ * grouping assigns head i to group g(i)).
+ *
+ *   q        [B, H, d_h]        the new queries
+ *   k_cache  [B, Tmax, G, d_h]  keys; position t of sequence b is k_cache[b, t]
+ *   v_cache  [B, Tmax, G, d_h]  values, same layout
+ *   seqlens  [B] int32, DEVICE memory: sequence b attends over positions
+ *            [0, L_b) with L_b = min(max(seqlens[b], 0), Tmax). Positions at or
+ *            beyond L_b are never read and may hold anything (NaN included).
+ *            L_b = 0 gives an all-zero output row. Whether the newest token's
+ *            key and value are among the L_b positions is the caller's choice.
+ *   scale    multiplies q.k before the softmax (1/sqrt(d_h) for the pages'
+ *            attention); must be finite.
+ *   out      [B, H, d_h]        same dtype as q
+ *   out[b,h,:] = sum_t softmax_t(scale * q[b,h,:].k_cache[b,t,g(h),:]) v_cache[b,t,g(h),:]
+ *
+ * Long sequences are split over workgroups and the pieces are merged with a
+ * log-sum-exp combine inside the same launch. The split workspace is owned by
+ * the library, one per (device, stream), allocated on first use with
+ * stream-ordered allocation and kept until the process ends.
+ * Requires 1 <= G, G divides H, Tmax >= 0, d_h in {64, 128}.
+ */
+gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens,
+                      int B, int H, int G, int d_h, int Tmax, float scale, gqa_dtype dtype, void *out,
+                      hipStream_t stream);
+
+/*
+ * gqa_decode_ex -- gqa_decode with an explicit split size: each workgroup
+ * takes at most `split_tokens` cache positions of one sequence (rounded up to
+ * a multiple of 32). 0 selects the size gqa_decode would use. Results agree
+ * with gqa_decode up to fp32 rounding of the combine. The fp32 path ignores
+ * split_tokens. Same source passages as gqa_decode.
+ */
+gqa_status gqa_decode_ex(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens,
+                         int B, int H, int G, int d_h, int Tmax, float scale, gqa_dtype dtype, void *out,
+                         hipStream_t stream, int split_tokens);
+
+/*
+ * gqa_prefill -- attention for every position of B sequences of length T.
+ * Defines: "Grouped-Query Attention" (llm-arch-kb), section 3 Reference
+ * implementation (sketch: q [B,T,H,d_h], k and v [B,T,G,d_h] broadcast to the
+ * H query heads group by group, scores divided by sqrt(d_h), causal mask,
+ * softmax over keys, times v).
+ *
+ *   q       [B, T, H, d_h]
+ *   k, v    [B, T, G, d_h]
+ *   causal  1: query position t attends to key positions s <= t (diagonal
+ *           kept); 0: to every position.
+ *   out     [B, T, H, d_h]   attention output before the output projection
+ *   The scale is fixed at 1/sqrt(d_h).
+ * Requires G divides H, T >= 0, d_h in {64, 128}.
+ */
+gqa_status gqa_prefill(const void *q, const void *k, const void *v, int B, int T, int H, int G, int d_h,
+                       int causal, gqa_dtype dtype, void *out, hipStream_t stream);
+
+/*
+ * gqa_mean_pool_kv -- convert multi-head key or value heads into G groups by
+ * averaging the r = H/G heads of each group.
+ * Defines: "Grouped-Query Attention" (llm-arch-kb), section 2 Derivation,
+ * Uptraining recipe (each group starts as the mean of the original heads
+ * assigned to it); crackai.dev paper card, How It Works (mean-pool the
+ * key/value heads within each group).
+ *
+ *   in   [N, H, d_h]  a weight matrix [d, H*d_h] viewed with N = d, or
+ *                     projected keys/values [tokens, H*d_h] with N = tokens
+ *   out  [N, G, d_h]  out[n,g,:] = (1/r) * sum_{j<r} in[n, g*r + j, :],
+ *                     accumulated in fp32; G = H copies exactly
+ * Requires G divides H, N >= 0, d_h >= 1 with d_h a multiple of 8.
+ */
+gqa_status gqa_mean_pool_kv(const void *in, int64_t N, int H, int G, int d_h, gqa_dtype dtype, void *out,
+                            hipStream_t stream);
+
+/*
+ * gqa_decode_plan -- the split plan gqa_decode_ex would use, computed on the
+ * host without touching the GPU: `chunk_tokens` positions per workgroup,
+ * `num_splits` = ceil(Tmax / chunk_tokens) workgroups per (sequence, group),
+ * and the workspace bytes the split combine needs (0 when num_splits is 1).
+ * `cu_count` is the GPU's compute-unit count (256 on MI355X). Any output
+ * pointer may be NULL. Returns GQA_OK or the status gqa_decode would return
+ * for the same sizes.
+ */
+gqa_status gqa_decode_plan(int B, int H, int G, int d_h, int Tmax, gqa_dtype dtype, int split_tokens,
+                           int cu_count, int *chunk_tokens, int *num_splits, int64_t *workspace_bytes);
+
+/* Short constant text for a status code. */
+const char *gqa_status_string(gqa_status s);
+
+/* Text of the last failure on the calling thread ("" if none). */
+const char *gqa_last_error(void);
+
+/* Library ABI version: 1. */
+int gqa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H_ */
