@@ -1,0 +1,285 @@
+"""Benchmark: GQA decode (headline) and causal GQA prefill on one MI355X.
+
+Prints ONE JSON line. A decode step is one gqa_decode call on the
+Llama-3-8B-shaped decode layer (B=16, H=32, G=8, d_h=128, every sequence at
+context 4096, bf16); `value` is whole-job decode throughput in GB/s of
+algorithmic bytes (K/V cache read + q read + out write + seqlens) over the
+wall-clock time of the timed steps. Prefill (B=4, T=8192, H=32, G=8,
+d_h=128, causal, bf16) is timed the same way and reported under "prefill"
+in TFLOP/s (2*B*H*T^2*d_h per call).
+
+Inputs are synthetic (seeded N(0,1), no datasets or weights) and resident in
+HBM before timing starts. Decode rotates through 4 input copies (1 GiB of
+K/V) so that no step can be served from the 256 MB MALL left warm by the
+step before it.
+
+roofline: per-launch kernel time from HIP events recorded on the stream the
+kernels run on (torch's current stream, which the library is handed).
+cpu_baseline: the fp64 CPU oracle timed on the host cores on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published (256 CU x 2.4 GHz x 4096 FLOP/clk)
+METRIC = "GQA decode HBM GB/s (% of peak) + causal prefill TFLOP/s (% MFMA peak), bf16"
+DECODE_WORKLOAD = "decode_llama3_8b"
+PREFILL_WORKLOAD = "prefill_llama3_8b_causal"
+KERNEL_SOURCES = {
+    "decode": ["grouped_query_kv_gqa_amd/csrc/decode.hip", "grouped_query_kv_gqa_amd/csrc/device_common.h"],
+    "prefill": ["grouped_query_kv_gqa_amd/csrc/prefill.hip", "grouped_query_kv_gqa_amd/csrc/device_common.h"],
+}
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kind: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on other kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_counters.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("source_hash") != source_hash(kind):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def decode_bytes(w, seqlens) -> int:
+    e = 2 if str(w.dtype).endswith("bfloat16") else 4
+    L = [min(max(int(x), 0), w.Tmax) for x in seqlens]
+    return sum(L) * w.G * w.D * 2 * e + 2 * w.B * w.H * w.D * e + 4 * w.B
+
+
+def prefill_flops(w) -> int:
+    return 2 * w.B * w.H * w.T * w.T * w.D
+
+
+def timed_launches(fn, steps, warmup, stream):
+    """Warm up, then time `steps` launches: per-launch HIP events on `stream`
+    and wall-clock around all of them (synchronised on both sides)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(a.elapsed_time(b) for a, b in ev)  # ms
+    return wall, per
+
+
+def pct(xs, q):
+    return xs[min(len(xs) - 1, int(q * len(xs)))]
+
+
+def run_decode(args):
+    import torch
+    import grouped_query_kv_gqa_amd as gq
+    from grouped_query_kv_gqa_amd import inputs as I
+
+    w = I.WORKLOADS[DECODE_WORKLOAD]
+    ncopy = 4
+    xs = [I.decode_inputs(w, seed=args.seed + c, device="cuda") for c in range(ncopy)]
+    outs = [torch.empty_like(x["q"]) for x in xs]
+    stream = torch.cuda.current_stream()
+    byts = decode_bytes(w, xs[0]["seqlens"].cpu().tolist())
+
+    def step(i):
+        x = xs[i % ncopy]
+        gq.decode(x["q"], x["k_cache"], x["v_cache"], x["seqlens"], scale=w.scale, out=outs[i % ncopy])
+
+    wall, per = timed_launches(step, args.steps, args.warmup, stream)
+    med = pct(per, 0.5)
+    mean = sum(per) / len(per)
+    res = {
+        "w": w, "bytes": byts, "wall": wall, "per_ms": per, "median_ms": med, "mean_ms": mean,
+        "plan": gq.decode_plan(w.B, w.H, w.G, w.D, w.Tmax),
+        "inputs": xs[0],
+    }
+    return res
+
+
+def run_prefill(args):
+    import torch
+    import grouped_query_kv_gqa_amd as gq
+    from grouped_query_kv_gqa_amd import inputs as I
+
+    w = I.PREFILL_WORKLOADS[PREFILL_WORKLOAD]
+    x = I.prefill_inputs(w, seed=args.seed, device="cuda")
+    out = torch.empty_like(x["q"])
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        gq.prefill(x["q"], x["k"], x["v"], causal=True, out=out)
+
+    wall, per = timed_launches(step, args.prefill_steps, args.prefill_warmup, stream)
+    return {"w": w, "flops": prefill_flops(w), "wall": wall, "per_ms": per, "median_ms": pct(per, 0.5),
+            "mean_ms": sum(per) / len(per), "inputs": x}
+
+
+def cpu_baseline_decode(res, budget_s):
+    """Oracle over whole sequences of the decode workload, repeated until
+    about `budget_s` seconds; GB/s of algorithmic bytes."""
+    import numpy as np
+    import oracle as O
+
+    w = res["w"]
+    x = res["inputs"]
+    cores = len(os.sched_getaffinity(0))
+    O.set_threads(cores)
+    q, k, v, sl = (x[n].cpu() for n in ("q", "k_cache", "v_cache", "seqlens"))
+    byts = decode_bytes(w, sl.tolist())
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        O.decode(q, k, v, sl.numpy(), w.scale)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(byts * reps / dt / 1e9, 3), "unit": "GB/s", "cores": O.max_threads(), "kind": "oracle",
+            "sample": f"whole {w.name} workload (B={w.B}, H={w.H}, G={w.G}, d_h={w.D}, L={w.Tmax}) "
+                      f"x{reps} in {dt:.1f} s, fp64"}
+
+
+def cpu_baseline_prefill(res, budget_s):
+    """Oracle on late rows of the prefill workload (the most expensive rows),
+    until about `budget_s` seconds; TFLOP/s counting 4*(t+1)*d_h per row."""
+    import numpy as np
+    import oracle as O
+
+    w = res["w"]
+    x = res["inputs"]
+    q, k, v = (x[n].cpu() for n in ("q", "k", "v"))
+    rng = np.random.default_rng(0)
+    done_flops, t0, rows = 0, time.perf_counter(), 0
+    while time.perf_counter() - t0 < budget_s:
+        n = 256
+        rb = rng.integers(0, w.B, n)
+        rt = rng.integers(w.T // 2, w.T, n)
+        rh = rng.integers(0, w.H, n)
+        O.prefill(q, k, v, causal=True, rows=(rb, rt, rh))
+        done_flops += int(sum(4 * (int(t) + 1) * w.D for t in rt))
+        rows += n
+    dt = time.perf_counter() - t0
+    return {"value": round(done_flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": O.max_threads(),
+            "kind": "oracle",
+            "sample": f"{rows} random causal rows with t in [T/2, T) of {w.name} in {dt:.1f} s, fp64"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--prefill-warmup", type=int, default=2)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds per CPU-baseline leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device-to-device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the decode and prefill kernels run on one GPU's share and no multi-GPU path exists",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")  # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    dec = run_decode(args)
+    w = dec["w"]
+    value = dec["bytes"] * args.steps / dec["wall"] / 1e9
+    kernel_gbs = dec["bytes"] / (dec["mean_ms"] * 1e-3) / 1e9
+    traffic = measured_traffic("decode")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["wall"] / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "G": w.G, "d_h": w.D, "context": w.Tmax,
+                   "seed": args.seed, "input_copies": 4, "split_plan": list(dec["plan"][:2])},
+        "roofline": {
+            "kernel": "decode_bf16_kernel",
+            "bound": "hbm",
+            "achieved": round(kernel_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": dec["bytes"],
+            "launch_ms": {"mean": round(dec["mean_ms"], 5), "median": round(dec["median_ms"], 5),
+                          "p10": round(pct(dec["per_ms"], 0.1), 5), "p90": round(pct(dec["per_ms"], 0.9), 5)},
+        },
+    }
+    if not args.no_prefill:
+        pf = run_prefill(args)
+        pw = pf["w"]
+        tflops = pf["flops"] / (pf["mean_ms"] * 1e-3) / 1e12
+        line["prefill"] = {
+            "workload": pw.name, "B": pw.B, "T": pw.T, "H": pw.H, "G": pw.G, "d_h": pw.D, "causal": True,
+            "value": round(pf["flops"] * args.prefill_steps / pf["wall"] / 1e12, 3), "unit": "TFLOP/s",
+            "steps": args.prefill_steps, "warmup": args.prefill_warmup,
+            "ms_per_step": round(pf["wall"] / args.prefill_steps * 1e3, 4),
+            "roofline": {"kernel": "prefill", "bound": "mfma", "achieved": round(tflops, 3),
+                         "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 5),
+                         "traffic": measured_traffic("prefill"), "flops_per_launch": pf["flops"],
+                         "launch_ms": {"mean": round(pf["mean_ms"], 4), "median": round(pf["median_ms"], 4)}},
+        }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_decode(dec, args.cpu_budget)
+        if "prefill" in line:
+            line["prefill"]["cpu_baseline"] = cpu_baseline_prefill(pf, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

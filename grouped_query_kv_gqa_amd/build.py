@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libgqa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
+COMMON = ["-O3", "-std=c++20", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
 # Device code: gfx950 only. Packed fp32 instructions are kept out of the
 # generated code (the host pass warns that it does not know the feature).
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

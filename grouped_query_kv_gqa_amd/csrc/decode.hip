@@ -6,28 +6,39 @@
 // entry is read at a decode step; section 2 Derivation, The grouping; section
 // 3 sketch, scaled scores, softmax over keys, times v).
 //
-// bf16 kernel design (memory-bound: every K/V byte is read exactly once):
-//  * Workgroup = (split of the sequence, key/value group g, sequence b); its
-//    waves walk 32-position tiles of the split round-robin and each wave keeps
-//    its own online-softmax state; the waves merge through LDS at the end.
-//  * All r = H/G query heads of the group share every K/V tile: the heads are
-//    the N dimension of 16x16x32 bf16 MFMAs, so one read of a tile serves the
-//    whole group.
+// bf16 design (HBM-bound: every K/V byte is read exactly once):
+//  * Work partition. The sequences' cache positions are laid end to end
+//    (sequence b owns flat positions [pre_b, pre_b + L_b)) and cut into equal
+//    pieces of P positions, P = ceil(sum_b L_b / workgroups) rounded up to 32,
+//    computed on the device from seqlens. Workgroup k takes flat positions
+//    [k P, (k+1) P), whatever sequences they belong to, so ragged batches and
+//    single long sequences balance the same way.
+//  * One workgroup covers GB adjacent key/value groups of its positions, one
+//    group per wave (or WAVES/GB waves per group that share its tiles). With
+//    GB = G = 8 every workgroup streams whole contiguous cache rows
+//    [t, 0:G, 0:d_h]; a workgroup per group would only touch one 256-byte
+//    slice of every 2 KiB row, which concentrates its traffic on a subset of
+//    memory channels and makes some groups markedly slower than others.
+//  * Within a wave, all r = H/G query heads of its group share every K/V tile:
+//    the heads are the N dimension of 16x16x32 bf16 MFMAs.
 //  * Scores: S^T[token, head] = K_tile . q^T. K goes from HBM straight into
 //    registers in the MFMA A layout (lane = token row, 16-byte chunk of d_h),
-//    q sits in registers as the B operand for the whole kernel.
+//    q sits in registers as the B operand.
 //  * The C layout of S^T (lane holds 4 tokens of one head) is already the B
 //    operand layout of P^T for O^T = V^T P^T, with tokens as the contraction
 //    index, so P never leaves registers.
 //  * V is loaded with fully coalesced 16-byte rows, written to a per-wave LDS
 //    tile, and read back with ds_read_b64_tr_b16, which delivers 4 consecutive
 //    tokens of one d column per lane: the A operand of V^T.
-//  * Softmax statistics are kept in base 2 (scores pre-multiplied by
-//    scale*log2(e)); row maxima use two cross-lane exchanges per tile.
-//  * A sequence longer than one split is spread over several workgroups; each
-//    writes a normalised partial row and its log-sum-exp, and the last
-//    workgroup to arrive for a (sequence, group, head tile) merges them, all
-//    in one launch.
+//  * Software pipeline with one register buffer each for K and V: the next
+//    tile's K is requested once this tile's scores are computed and its V
+//    once this tile's V sits in LDS, so both overlap the softmax and P.V.
+//  * Online softmax in base 2 (scores pre-multiplied by scale*log2(e)); row
+//    maxima use two cross-lane exchanges per tile.
+//  * A sequence that lies wholly inside one wave's piece is written to `out`
+//    directly. Otherwise each piece writes a normalised fp32 partial row and
+//    its base-2 log-sum-exp, and a second, small kernel merges the partials of
+//    every row (the kernel boundary orders the two; no atomics are used).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -37,8 +48,8 @@ namespace {
 
 constexpr int kTile = 32;  // positions per wave iteration
 
-template <int D, int NT, int WAVES>
-struct DecodeCfg {
+template <int D, int NT>
+struct TileCfg {
     static constexpr int KS = D / 32;          // MFMA k-steps over d_h
     static constexpr int DT = D / 16;          // 16-wide d tiles of the output
     static constexpr int CH = D / 8;           // 16-byte chunks per row
@@ -46,10 +57,6 @@ struct DecodeCfg {
     static constexpr int VLOADS = kTile / VROWS;
     static constexpr int LDS_STRIDE = D + 16;  // padded row (elements): 4 rows cover all banks
     static constexpr int HEADS = 16 * NT;
-    static constexpr int V_LDS_ELEMS = WAVES * kTile * LDS_STRIDE;
-    // merge area (floats) aliases the V tiles after the main loop
-    static constexpr int RED_FLOATS = HEADS * D + 2 * WAVES * HEADS;
-    static constexpr int LDS_BYTES = (V_LDS_ELEMS * 2 > RED_FLOATS * 4) ? V_LDS_ELEMS * 2 : RED_FLOATS * 4;
 };
 
 __device__ __forceinline__ u32x4_t load16(const __bf16 *p)
@@ -57,42 +64,65 @@ __device__ __forceinline__ u32x4_t load16(const __bf16 *p)
     return *reinterpret_cast<const u32x4_t *>(p);
 }
 
-template <int D, int NT, int WAVES>
-__global__ void __launch_bounds__(WAVES * 64)
-decode_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kc, const __bf16 *__restrict__ vc,
-                   const int32_t *__restrict__ seqlens, int H, int G, int Tmax, int r, int head_tiles,
-                   float scale_log2, int chunk, int splits, __bf16 *__restrict__ out,
-                   float *__restrict__ part, float *__restrict__ lse, int *__restrict__ counters)
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t x)
 {
-    using C = DecodeCfg<D, NT, WAVES>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS_BYTES];
-    __shared__ int s_last;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        x += __shfl_xor(x, m, 64);
+    return x;
+}
 
-    const int split = blockIdx.x;
-    const int g = blockIdx.y / head_tiles;
-    const int ht = blockIdx.y % head_tiles;
-    const int b = blockIdx.z;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int col = lane & 15, kb = lane >> 4;
-
-    const int L = clamp_len(seqlens[b], Tmax);
-    const int t_begin = split * chunk;
-    const int n_active = (L + chunk - 1) / chunk;
-    const int h0 = g * r + ht * C::HEADS;                  // first query head of this tile
-    const int nheads = min(C::HEADS, r - ht * C::HEADS);   // valid heads in this tile
-    const int64_t row0 = (int64_t)b * H + h0;              // first output row
-
-    if (t_begin >= L) {
-        if (split == 0) {  // empty sequence: zero rows
-            for (int i = tid; i < nheads * C::CH; i += WAVES * 64) {
-                const int hh = i / C::CH, c = i % C::CH;
-                *reinterpret_cast<u32x4_t *>(out + (row0 + hh) * D + c * 8) = (u32x4_t){0, 0, 0, 0};
-            }
-        }
-        return;
+__device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t x, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int64_t y = __shfl_up(x, (unsigned)d, 64);
+        if (lane >= d)
+            x += y;
     }
-    const int t_end = min(t_begin + chunk, L);
+    return x;
+}
+
+// Flat-position partition shared by the decode and merge kernels (both must
+// compute identical values): total positions and the piece length P.
+struct Partition {
+    int64_t total;
+    int64_t P;
+};
+
+__device__ __forceinline__ Partition make_partition(const int32_t *seqlens, int B, int Tmax, int nwg, int fixed_P,
+                                                    int lane)
+{
+    int64_t tot = 0;
+    for (int i = lane; i < B; i += 64)
+        tot += clamp_len(seqlens[i], Tmax);
+    tot = wave_sum_i64(tot);
+    int64_t P;
+    if (fixed_P > 0) {
+        P = fixed_P;
+    } else {
+        P = (tot + nwg - 1) / nwg;
+        P = ((P + kTile - 1) / kTile) * kTile;
+        if (P < kTile)
+            P = kTile;
+    }
+    return {tot, P};
+}
+
+// One wave's work on one piece: positions [ta, tb) of sequence b for the
+// heads [h0, h0 + nheads) of group g. The wave takes tiles ta + sub*32,
+// ta + (sub + WPG)*32, ... Writes the finished rows to `out` when `whole`,
+// else a normalised partial row per head and its base-2 log-sum-exp.
+template <int D, int NT, int WPG>
+__device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, const __bf16 *kc, const __bf16 *vc,
+                                             int b, int g, int h0, int nheads, int ta, int tb, bool whole, int H,
+                                             int G, int Tmax, int sub, float scale_log2, __bf16 *vl,
+                                             __bf16 *__restrict__ out, float *__restrict__ part_row,
+                                             float *__restrict__ lse_row, int64_t part_stride, int lane)
+{
+    using C = TileCfg<D, NT>;
+    const int col = lane & 15, kb = lane >> 4;
+    const int64_t row0 = (int64_t)b * H + h0;
 
     // q as the MFMA B operand: column = head, k = d chunk (4*s + kb).
     bf16x8_t qf[NT][C::KS];
@@ -111,7 +141,6 @@ decode_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kc, 
     const int64_t tok_stride = (int64_t)G * D;
     const __bf16 *kbase = kc + ((int64_t)b * Tmax * G + g) * D;
     const __bf16 *vbase = vc + ((int64_t)b * Tmax * G + g) * D;
-    __bf16 *vl = reinterpret_cast<__bf16 *>(smem) + wave * kTile * C::LDS_STRIDE;
 
     float m_run[NT], l_run[NT];
     f32x4_t acc[NT][C::DT];
@@ -124,45 +153,43 @@ decode_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kc, 
             acc[nt][dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     }
 
-    u32x4_t kcur[2][C::KS], vcur[C::VLOADS];
-    auto load_tile = [&](int t0, u32x4_t (&kr)[2][C::KS], u32x4_t (&vr)[C::VLOADS]) {
+    // Loads are unconditional: rows past the piece are clamped to its last
+    // row, and the values they bring are discarded below (scores set to -inf,
+    // V rows replaced by zeros). Keeping per-lane branches away from loads
+    // lets the compiler wait for exactly the data it needs.
+    const int t_last = tb - 1;
+    auto load_k = [&](int t0, u32x4_t (&kr)[2][C::KS]) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-            const int t = t0 + mt * 16 + col;
+            const int t = min(t0 + mt * 16 + col, t_last);
 #pragma unroll
-            for (int s = 0; s < C::KS; ++s) {
-                u32x4_t v = {0, 0, 0, 0};
-                if (t < t_end)
-                    v = load16(kbase + t * tok_stride + (s * 4 + kb) * 8);
-                kr[mt][s] = v;
-            }
+            for (int s = 0; s < C::KS; ++s)
+                kr[mt][s] = load16(kbase + t * tok_stride + (s * 4 + kb) * 8);
         }
+    };
+    auto load_v = [&](int t0, u32x4_t (&vr)[C::VLOADS]) {
 #pragma unroll
         for (int i = 0; i < C::VLOADS; ++i) {
-            const int t = t0 + i * C::VROWS + lane / C::CH;
-            u32x4_t v = {0, 0, 0, 0};
-            if (t < t_end)
-                v = load16(vbase + t * tok_stride + (lane % C::CH) * 8);
-            vr[i] = v;
+            const int t = min(t0 + i * C::VROWS + lane / C::CH, t_last);
+            vr[i] = load16(vbase + t * tok_stride + (lane % C::CH) * 8);
         }
     };
 
-    int t0 = t_begin + wave * kTile;
-    if (t0 < t_end)
-        load_tile(t0, kcur, vcur);
-    while (t0 < t_end) {
-        const int tn = t0 + WAVES * kTile;
-        u32x4_t knext[2][C::KS], vnext[C::VLOADS];
-        if (tn < t_end)
-            load_tile(tn, knext, vnext);
-
-        // V tile into this wave's LDS rows (natural [token][d] order).
-        compiler_fence();
-#pragma unroll
-        for (int i = 0; i < C::VLOADS; ++i)
-            *reinterpret_cast<u32x4_t *>(vl + (i * C::VROWS + lane / C::CH) * C::LDS_STRIDE + (lane % C::CH) * 8) =
-                vcur[i];
-        compiler_fence();
+    // Software pipeline with one K and one V register buffer: the next K is
+    // requested as soon as this tile's scores have consumed K, the next V as
+    // soon as this tile's V is in LDS; both arrive while the softmax and P.V
+    // of this tile run. The K/V pointers are deliberately not __restrict__
+    // (with it the loads count as invariant and get moved across the fences
+    // below), and the scheduling barriers keep each request at its place.
+    int t0 = ta + sub * kTile;
+    const bool any_tile = t0 < tb;  // wave-uniform
+    u32x4_t kbuf[2][C::KS], vbuf[C::VLOADS];
+    if (any_tile) {
+        load_k(t0, kbuf);
+        load_v(t0, vbuf);
+    }
+    while (any_tile) {
+        const int tn = t0 + WPG * kTile;
 
         // S^T = K q^T for two 16-token row tiles.
         f32x4_t st[2][NT];
@@ -173,9 +200,29 @@ decode_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kc, 
                 f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < C::KS; ++s)
-                    c = mfma16x16x32(__builtin_bit_cast(bf16x8_t, kcur[mt][s]), qf[nt][s], c);
+                    c = mfma16x16x32(__builtin_bit_cast(bf16x8_t, kbuf[mt][s]), qf[nt][s], c);
                 st[mt][nt] = c;
             }
+        compiler_fence();
+        __builtin_amdgcn_sched_barrier(0);
+        load_k(tn, kbuf);  // clamped prefetch, also past the end
+        compiler_fence();
+        __builtin_amdgcn_sched_barrier(0);
+
+        // V tile into this wave's LDS rows (natural [token][d] order); rows
+        // past the piece become zeros so that p = 0 never meets a NaN.
+#pragma unroll
+        for (int i = 0; i < C::VLOADS; ++i) {
+            const int tl = i * C::VROWS + lane / C::CH;
+            const u32x4_t zero = {0, 0, 0, 0};
+            *reinterpret_cast<u32x4_t *>(vl + tl * C::LDS_STRIDE + (lane % C::CH) * 8) =
+                (t0 + tl < tb) ? vbuf[i] : zero;
+        }
+        compiler_fence();
+        __builtin_amdgcn_sched_barrier(0);
+        load_v(tn, vbuf);
+        compiler_fence();
+        __builtin_amdgcn_sched_barrier(0);
 
         // Online softmax (base 2). Lane holds tokens t0 + 16*mt + 4*kb + i of head column col.
         bf16x8_t pf[NT];
@@ -187,7 +234,7 @@ decode_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kc, 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int t = t0 + mt * 16 + kb * 4 + i;
-                    const float x = (t < t_end) ? st[mt][nt][i] * scale_log2 : -INFINITY;
+                    const float x = (t < tb) ? st[mt][nt][i] * scale_log2 : -INFINITY;
                     st[mt][nt][i] = x;
                     mx = fmaxf(mx, x);
                 }
@@ -227,152 +274,238 @@ decode_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kc, 
                 acc[nt][dt] = mfma16x16x32(vf, pf[nt], acc[nt][dt]);
         }
 
-        if (tn < t_end) {
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int s = 0; s < C::KS; ++s)
-                    kcur[mt][s] = knext[mt][s];
-#pragma unroll
-            for (int i = 0; i < C::VLOADS; ++i)
-                vcur[i] = vnext[i];
-        }
+        if (tn >= tb)
+            break;
         t0 = tn;
     }
 
-    // ---- merge the waves of this workgroup -------------------------------
+    // Finish: the four lanes of one head column hold disjoint token subsets'
+    // weight sums; the accumulator lane holds O^T[dt*16 + 4*kb + i][head].
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         l_run[nt] += __shfl_xor(l_run[nt], 16, 64);
         l_run[nt] += __shfl_xor(l_run[nt], 32, 64);
     }
-    __syncthreads();  // every wave is done with its V tile
-    float *red = reinterpret_cast<float *>(smem);          // [HEADS][D]
-    float *wm = red + C::HEADS * D;                         // [WAVES][HEADS]
-    float *wl = wm + WAVES * C::HEADS;                      // [WAVES][HEADS]
-    if (kb == 0) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            wm[wave * C::HEADS + nt * 16 + col] = m_run[nt];
-            wl[wave * C::HEADS + nt * 16 + col] = l_run[nt];
-        }
-    }
-    __syncthreads();
-    // Wave w adds its rescaled accumulator after waves 0..w-1 (fixed order,
-    // so repeated launches give identical bits).
-    float f[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int hh = nt * 16 + col;
-        float M = -INFINITY;
+        if (hh >= nheads)
+            continue;
+        const float inv = l_run[nt] > 0.f ? 1.f / l_run[nt] : 0.f;
+        if (whole) {
+            __bf16 *dst = out + (row0 + hh) * D + kb * 4;
 #pragma unroll
-        for (int w = 0; w < WAVES; ++w)
-            M = fmaxf(M, wm[w * C::HEADS + hh]);
-        f[nt] = (m_run[nt] == -INFINITY) ? 0.f : fast_exp2(m_run[nt] - M);
-    }
-    for (int w = 0; w < WAVES; ++w) {
-        if (wave == w) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int hh = nt * 16 + col;
-                if (hh < nheads) {
-#pragma unroll
-                    for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            float *dst = &red[hh * D + dt * 16 + kb * 4 + i];
-                            const float x = acc[nt][dt][i] * f[nt];
-                            *dst = (w == 0) ? x : *dst + x;
-                        }
-                }
+            for (int dt = 0; dt < C::DT; ++dt) {
+                const f32x4_t o = acc[nt][dt] * inv;
+                u32x2_t u = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                *reinterpret_cast<u32x2_t *>(dst + dt * 16) = u;
             }
+        } else {
+            float *dst = part_row + hh * part_stride * D + kb * 4;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt)
+                *reinterpret_cast<f32x4_t *>(dst + dt * 16) = acc[nt][dt] * inv;
+            if (kb == 0)
+                lse_row[hh * part_stride] = l_run[nt] > 0.f ? m_run[nt] + fast_log2(l_run[nt]) : -INFINITY;
         }
-        __syncthreads();
+    }
+}
+
+template <int D, int NT, int WAVES, int GB>
+__global__ void __launch_bounds__(WAVES * 64)
+decode_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kc, const __bf16 *vc,
+                   const int32_t *__restrict__ seqlens, int B, int H, int G, int Tmax, int r, int head_tiles,
+                   float scale_log2, int nwg, int fixed_P, __bf16 *__restrict__ out, float *__restrict__ part,
+                   float *__restrict__ lse)
+{
+    constexpr int WPG = WAVES / GB;
+    using C = TileCfg<D, NT>;
+    __shared__ __attribute__((aligned(16))) __bf16 vlds[WAVES][kTile * C::LDS_STRIDE];
+
+    const int k = blockIdx.x;
+    const int gblk = blockIdx.y / head_tiles;
+    const int ht = blockIdx.y % head_tiles;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = gblk * GB + wave / WPG;
+    const int sub = wave % WPG;
+    const int h0 = g * r + ht * C::HEADS;
+    const int nheads = min(C::HEADS, r - ht * C::HEADS);
+
+    const Partition pt = make_partition(seqlens, B, Tmax, nwg, fixed_P, lane);
+    const int64_t lo = (int64_t)k * pt.P;
+    if (lo >= pt.total)
+        return;
+    const int64_t hi = min(lo + pt.P, pt.total);
+
+    // Walk the sequences overlapping [lo, hi), 64 lengths at a time.
+    int64_t pre = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+        const int Lc = (b0 + lane < B) ? clamp_len(seqlens[b0 + lane], Tmax) : 0;
+        const int64_t incl = wave_incl_scan_i64(Lc, lane);
+        const int64_t chunk_total = __shfl(incl, 63, 64);
+        if (pre + chunk_total <= lo) {
+            pre += chunk_total;
+            continue;
+        }
+        const int n = min(64, B - b0);
+        for (int i = 0; i < n; ++i) {
+            const int L = __shfl(Lc, i, 64);
+            const int64_t pre_b = pre + __shfl(incl, i, 64) - L;
+            if (pre_b >= hi)
+                return;
+            if (L == 0 || pre_b + L <= lo)
+                continue;
+            const int b = b0 + i;
+            const int ta = (int)max<int64_t>(lo - pre_b, 0);
+            const int tb = (int)min<int64_t>(hi - pre_b, L);
+            const bool whole = (WPG == 1) && ta == 0 && tb == L;
+            const int64_t piece = (int64_t)k + b;
+            // partial layout [piece][head][sub][d], log-sum-exp [piece][head][sub]
+            const int64_t slot = (piece * H + h0) * WPG + sub;
+            decode_piece<D, NT, WPG>(q, kc, vc, b, g, h0, nheads, ta, tb, whole, H, G, Tmax, sub, scale_log2,
+                                     &vlds[wave][0], out, part + slot * D, lse + slot, WPG, lane);
+        }
+        pre += chunk_total;
+    }
+}
+
+// Merge of the partial rows. Workgroup = (block of 4 row items, sequence b):
+// its 256 threads compute the partition once; each wave then merges one item
+// = (head h, NQ*4 consecutive d). Lanes form 64/NQ slot lanes x NQ d-quads:
+// slot lane sl takes the row's pieces sl, sl + 64/NQ, ... and the lanes of a
+// d-quad are combined with shuffles. out = sum_j w_j o_j with
+// w_j = 2^(lse_j - M) / sum_j' 2^(lse_j' - M). Also writes the zero rows of
+// empty sequences; rows that the decode kernel wrote whole are skipped.
+template <int D, int NQ>
+__global__ void __launch_bounds__(256)
+decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax, int nwg, int fixed_P, int wpg,
+                    const float *__restrict__ part, const float *__restrict__ lse, __bf16 *__restrict__ out)
+{
+    constexpr int DCH = 4 * NQ;      // d values per item
+    constexpr int NDC = D / DCH;     // items per row
+    constexpr int NS = 64 / NQ;      // slot lanes
+    __shared__ int64_t s_red[2][4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = blockIdx.y;
+
+    // partition and this sequence's first flat position, once per workgroup
+    int64_t tot = 0, pre = 0;
+    for (int i = tid; i < B; i += 256) {
+        const int Li = clamp_len(seqlens[i], Tmax);
+        tot += Li;
+        if (i < b)
+            pre += Li;
+    }
+    tot = wave_sum_i64(tot);
+    pre = wave_sum_i64(pre);
+    if (lane == 0) {
+        s_red[0][wave] = tot;
+        s_red[1][wave] = pre;
+    }
+    __syncthreads();
+    tot = s_red[0][0] + s_red[0][1] + s_red[0][2] + s_red[0][3];
+    const int64_t pre_b = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
+    int64_t P;
+    if (fixed_P > 0) {
+        P = fixed_P;
+    } else {
+        P = (tot + nwg - 1) / nwg;
+        P = ((P + kTile - 1) / kTile) * kTile;
+        if (P < kTile)
+            P = kTile;
     }
 
-    // Per-head totals of this workgroup: max M and sum l scaled to M.
-    auto head_stats = [&](int hh, float &M, float &Ls) {
-        M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w)
-            M = fmaxf(M, wm[w * C::HEADS + hh]);
-        Ls = 0.f;
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) {
-            const float mw = wm[w * C::HEADS + hh];
-            if (mw != -INFINITY)
-                Ls += wl[w * C::HEADS + hh] * fast_exp2(mw - M);
-        }
-    };
-
-    if (n_active == 1) {  // the whole sequence was in this workgroup
-        for (int i = tid; i < nheads * C::CH; i += WAVES * 64) {
-            const int hh = i / C::CH, c = i % C::CH;
-            float M, Ls;
-            head_stats(hh, M, Ls);
-            const float inv = 1.f / Ls;
-            const float *src = red + hh * D + c * 8;
-            u32x4_t o;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                o[j] = pack_bf16x2(src[2 * j] * inv, src[2 * j + 1] * inv);
-            *reinterpret_cast<u32x4_t *>(out + (row0 + hh) * D + c * 8) = o;
-        }
+    const int item = blockIdx.x * 4 + wave;
+    if (item >= H * NDC)
+        return;
+    const int h = item / NDC, dc = item % NDC;
+    const int sl = lane / NQ, qd = lane % NQ;
+    const int d0 = dc * DCH + qd * 4;
+    __bf16 *dst = out + ((int64_t)b * H + h) * D + d0;
+    const int L = clamp_len(seqlens[b], Tmax);
+    if (L == 0) {
+        if (sl == 0)
+            *reinterpret_cast<u32x2_t *>(dst) = (u32x2_t){0, 0};
         return;
     }
+    const int64_t k_first = pre_b / P;
+    const int64_t k_last = (pre_b + L - 1) / P;
+    if (k_first == k_last && wpg == 1)
+        return;  // written whole by the decode kernel
+    const int nslots = (int)(k_last - k_first + 1) * wpg;
 
-    // Several workgroups share this sequence: write a normalised partial row
-    // and its base-2 log-sum-exp.
-    for (int i = tid; i < nheads * (D / 4); i += WAVES * 64) {
-        const int hh = i / (D / 4), c = i % (D / 4);
-        float M, Ls;
-        head_stats(hh, M, Ls);
-        const float inv = 1.f / Ls;
-        const float *src = red + hh * D + c * 4;
-        f32x4_t o = {src[0] * inv, src[1] * inv, src[2] * inv, src[3] * inv};
-        *reinterpret_cast<f32x4_t *>(part + ((row0 + hh) * splits + split) * D + c * 4) = o;
-        if (c == 0)
-            lse[(row0 + hh) * splits + split] = M + fast_log2(Ls);
-    }
-    __threadfence();
-    __syncthreads();
-    const int pair = (b * G + g) * head_tiles + ht;
-    if (tid == 0) {
-        const int prev = atomicAdd(&counters[pair], 1);
-        s_last = (prev == n_active - 1);
-    }
-    __syncthreads();
-    if (!s_last)
-        return;
-    __threadfence();
-
-    // Last arrival: merge the n_active partial rows of every head.
-    for (int i = tid; i < nheads * C::CH; i += WAVES * 64) {
-        const int hh = i / C::CH, c = i % C::CH;
-        const int64_t row = row0 + hh;
-        const float *lrow = lse + row * splits;
-        float M = -INFINITY;
-        for (int s = 0; s < n_active; ++s)
-            M = fmaxf(M, lrow[s]);
-        float den = 0.f;
-        f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < n_active; ++s) {
-            const float w = fast_exp2(lrow[s] - M);
-            const f32x4_t *src = reinterpret_cast<const f32x4_t *>(part + (row * splits + s) * D + c * 8);
-            a0 += w * src[0];
-            a1 += w * src[1];
+    float m = -INFINITY, den = 0.f;
+    f32x4_t num = {0.f, 0.f, 0.f, 0.f};
+    constexpr int U = 4;  // slots per lane per round, loads issued together
+    for (int j0 = sl; j0 < nslots; j0 += NS * U) {
+        float x[U];
+        f32x4_t pv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = min(j0 + NS * u, nslots - 1);
+            const int64_t piece = k_first + j / wpg + b;
+            const int64_t idx = (piece * H + h) * wpg + j % wpg;
+            x[u] = lse[idx];
+            pv[u] = *reinterpret_cast<const f32x4_t *>(part + idx * D + d0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (j0 + NS * u >= nslots || x[u] == -INFINITY)
+                continue;
+            if (x[u] > m) {
+                const float f = fast_exp2(m - x[u]);
+                den *= f;
+                num *= f;
+                m = x[u];
+            }
+            const float w = fast_exp2(x[u] - m);
             den += w;
+            num += w * pv[u];
         }
-        const float inv = 1.f / den;
-        u32x4_t o;
-        o[0] = pack_bf16x2(a0[0] * inv, a0[1] * inv);
-        o[1] = pack_bf16x2(a0[2] * inv, a0[3] * inv);
-        o[2] = pack_bf16x2(a1[0] * inv, a1[1] * inv);
-        o[3] = pack_bf16x2(a1[2] * inv, a1[3] * inv);
-        *reinterpret_cast<u32x4_t *>(out + row * D + c * 8) = o;
     }
-    if (tid == 0)
-        atomicExch(&counters[pair], 0);  // ready for the next launch
+    // combine the slot lanes of each d-quad (lanes qd, qd + NQ, ...)
+    float M = m;
+#pragma unroll
+    for (int s = 32; s >= NQ; s >>= 1)
+        M = wave_max_xor(M, s);
+    const float f = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
+    den *= f;
+    num *= f;
+#pragma unroll
+    for (int s = 32; s >= NQ; s >>= 1) {
+        den += __shfl_xor(den, s, 64);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            num[e] += __shfl_xor(num[e], s, 64);
+    }
+    if (sl == 0) {
+        const float inv = 1.f / den;
+        u32x2_t u = {pack_bf16x2(num[0] * inv, num[1] * inv), pack_bf16x2(num[2] * inv, num[3] * inv)};
+        *reinterpret_cast<u32x2_t *>(dst) = u;
+    }
+}
+
+template <int D, int NQ>
+hipError_t launch_merge(const DecodePlan &p, const DecodeArgs &a, int wpg)
+{
+    constexpr int NDC = D / (4 * NQ);
+    dim3 grid((unsigned)((a.H * NDC + 3) / 4), (unsigned)a.B);
+    decode_merge_kernel<D, NQ><<<grid, 256, 0, a.stream>>>(a.seqlens, a.B, a.H, a.Tmax, p.nwg, p.fixed_P, wpg,
+                                                          a.part, a.lse, static_cast<__bf16 *>(a.out));
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_merge_d(const DecodePlan &p, const DecodeArgs &a, int wpg)
+{
+    switch (p.merge_nq) {
+    case 1: return launch_merge<D, 1>(p, a, wpg);
+    case 2: return launch_merge<D, 2>(p, a, wpg);
+    case 4: return launch_merge<D, 4>(p, a, wpg);
+    case 8: return launch_merge<D, 8>(p, a, wpg);
+    case 16: return launch_merge<D, 16>(p, a, wpg);
+    default: return launch_merge<D, (D >= 128 ? 32 : 16)>(p, a, wpg);
+    }
 }
 
 // fp32 debug path: one wavefront per (sequence, head); lanes split d_h and the
@@ -418,28 +551,52 @@ decode_f32_kernel(const float *__restrict__ q, const float *__restrict__ kc, con
         out[row * D + lane + 64 * j] = L > 0 ? acc[j] / l : 0.f;
 }
 
-template <int D, int NT, int WAVES>
-hipError_t launch_bf16(const DecodePlan &p, const DecodeArgs &a)
+template <int D, int NT, int WAVES, int GB>
+const void *bf16_symbol()
 {
-    dim3 grid(p.splits, a.G * p.head_tiles, a.B);
-    decode_bf16_kernel<D, NT, WAVES><<<grid, WAVES * 64, 0, a.stream>>>(
-        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), static_cast<const __bf16 *>(a.v),
-        a.seqlens, a.H, a.G, a.Tmax, p.r, p.head_tiles, a.scale * kLog2e, p.chunk, p.splits,
-        static_cast<__bf16 *>(a.out), a.part, a.lse, a.counters);
-    return hipGetLastError();
+    return reinterpret_cast<const void *>(&decode_bf16_kernel<D, NT, WAVES, GB>);
 }
 
-template <int D>
-hipError_t launch_bf16_d(const DecodePlan &p, const DecodeArgs &a)
+template <int D, int NT, int WAVES, int GB>
+hipError_t launch_bf16(const DecodePlan &p, const DecodeArgs &a)
 {
-    switch (p.nt) {
-    case 1: return launch_bf16<D, 1, 4>(p, a);
-    case 2: return launch_bf16<D, 2, 4>(p, a);
-    default: return launch_bf16<D, 4, 4>(p, a);
-    }
+    dim3 grid(p.nwg, (a.G / GB) * p.head_tiles);
+    decode_bf16_kernel<D, NT, WAVES, GB><<<grid, WAVES * 64, 0, a.stream>>>(
+        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), static_cast<const __bf16 *>(a.v),
+        a.seqlens, a.B, a.H, a.G, a.Tmax, p.r, p.head_tiles, a.scale * kLog2e, p.nwg, p.fixed_P,
+        static_cast<__bf16 *>(a.out), a.part, a.lse);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    return launch_merge_d<D>(p, a, WAVES / GB);
+}
+
+// Dispatch over the compiled variants: (d_h, head tiles NT, waves, groups per workgroup GB).
+template <typename F>
+hipError_t with_variant(const DecodePlan &p, int D, F &&f)
+{
+#define GQA_VARIANT(DD, NTT, WW, GG)                                       \
+    if (D == DD && p.nt == NTT && p.waves == WW && p.gb == GG)             \
+        return f.template operator()<DD, NTT, WW, GG>();
+#define GQA_VARIANTS(DD)                                                    \
+    GQA_VARIANT(DD, 1, 8, 8) GQA_VARIANT(DD, 1, 8, 4) GQA_VARIANT(DD, 1, 8, 2) GQA_VARIANT(DD, 1, 8, 1) \
+    GQA_VARIANT(DD, 2, 4, 4) GQA_VARIANT(DD, 2, 4, 2) GQA_VARIANT(DD, 2, 4, 1)                        \
+    GQA_VARIANT(DD, 4, 4, 4) GQA_VARIANT(DD, 4, 4, 2) GQA_VARIANT(DD, 4, 4, 1)
+    GQA_VARIANTS(64)
+    GQA_VARIANTS(128)
+#undef GQA_VARIANTS
+#undef GQA_VARIANT
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
+
+hipError_t decode_blocks_per_cu(const DecodePlan &p, int D, int *blocks)
+{
+    return with_variant(p, D, [&]<int DD, int NTT, int WW, int GG>() {
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, bf16_symbol<DD, NTT, WW, GG>(), WW * 64, 0);
+    });
+}
 
 hipError_t launch_decode(const DecodePlan &p, const DecodeArgs &a, gqa_dtype dtype)
 {
@@ -455,7 +612,7 @@ hipError_t launch_decode(const DecodePlan &p, const DecodeArgs &a, gqa_dtype dty
                 a.seqlens, a.H, a.G, a.Tmax, p.r, a.scale, static_cast<float *>(a.out));
         return hipGetLastError();
     }
-    return a.D == 64 ? launch_bf16_d<64>(p, a) : launch_bf16_d<128>(p, a);
+    return with_variant(p, a.D, [&]<int DD, int NTT, int WW, int GG>() { return launch_bf16<DD, NTT, WW, GG>(p, a); });
 }
 
 }  // namespace gqa

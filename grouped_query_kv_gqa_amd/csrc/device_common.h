@@ -84,6 +84,13 @@ __device__ __forceinline__ int clamp_len(int32_t L, int Tmax)
     return L < 0 ? 0 : (L > Tmax ? Tmax : (int)L);
 }
 
+// Wait until every vector memory operation this wave issued has completed
+// (stores acknowledged): s_waitcnt vmcnt(0) with expcnt and lgkmcnt left free.
+__device__ __forceinline__ void wait_vector_memory()
+{
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 // Compiler-level ordering point for memory operations of one wave.
 __device__ __forceinline__ void compiler_fence()
 {

@@ -33,7 +33,6 @@ gqa_status hip_failure(hipError_t e, const char *where)
 struct Workspace {
     char *ptr = nullptr;
     int64_t bytes = 0;
-    int64_t zeroed_counters = 0;  // counters [0, zeroed_counters) are known to be zero
 };
 
 struct Key {
@@ -52,6 +51,7 @@ struct KeyHash {
 std::mutex g_mutex;
 std::unordered_map<Key, Workspace, KeyHash> g_workspaces;
 std::unordered_map<int, int> g_cu_count;
+std::unordered_map<int64_t, int> g_blocks_per_cu;  // (device, d_h, nt, waves, gb) -> workgroups per CU
 
 gqa_status cu_count(int device, int *out)
 {
@@ -69,13 +69,33 @@ gqa_status cu_count(int device, int *out)
     return GQA_OK;
 }
 
-// Returns a workspace of at least plan.workspace_bytes whose first
-// plan.n_counters int32 counters are zero when the queued work reaches them.
-gqa_status workspace_for(int device, hipStream_t stream, const gqa::DecodePlan &plan, char **out)
+gqa_status blocks_per_cu(int device, const gqa::DecodePlan &p, int d_h, int *out)
+{
+    const int64_t key = ((((int64_t)device * 256 + d_h) * 8 + p.nt) * 16 + p.waves) * 16 + p.gb;
+    auto it = g_blocks_per_cu.find(key);
+    if (it != g_blocks_per_cu.end()) {
+        *out = it->second;
+        return GQA_OK;
+    }
+    int n = 0;
+    hipError_t e = gqa::decode_blocks_per_cu(p, d_h, &n);
+    if (e != hipSuccess)
+        return hip_failure(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    if (n < 1)
+        n = 1;
+    g_blocks_per_cu[key] = n;
+    *out = n;
+    return GQA_OK;
+}
+
+// A workspace of at least `bytes` for this (device, stream). Growth frees the
+// old block in stream order, so work already queued on the stream still sees
+// valid memory.
+gqa_status workspace_for(int device, hipStream_t stream, int64_t bytes, char **out)
 {
     Workspace &ws = g_workspaces[Key{device, stream}];
-    hipError_t e;
-    if (ws.bytes < plan.workspace_bytes) {
+    if (ws.bytes < bytes) {
+        hipError_t e;
         if (ws.ptr) {
             e = hipFreeAsync(ws.ptr, stream);
             if (e != hipSuccess)
@@ -83,21 +103,12 @@ gqa_status workspace_for(int device, hipStream_t stream, const gqa::DecodePlan &
             ws.ptr = nullptr;
             ws.bytes = 0;
         }
-        int64_t bytes = plan.workspace_bytes + plan.workspace_bytes / 4;  // headroom for growth
-        e = hipMallocAsync(reinterpret_cast<void **>(&ws.ptr), static_cast<size_t>(bytes), stream);
+        const int64_t grown = bytes + bytes / 4;  // headroom for growth
+        e = hipMallocAsync(reinterpret_cast<void **>(&ws.ptr), static_cast<size_t>(grown), stream);
         if (e != hipSuccess)
             return hip_failure(e, "hipMallocAsync");
-        ws.bytes = bytes;
-        ws.zeroed_counters = 0;
+        ws.bytes = grown;
     }
-    if (ws.zeroed_counters < plan.n_counters) {
-        e = gqa::launch_fill_i32(reinterpret_cast<int *>(ws.ptr + plan.counter_offset), plan.n_counters, 0, stream);
-        if (e != hipSuccess)
-            return hip_failure(e, "zero counters");
-    }
-    // Partial rows start right after this call's counters, so counters past
-    // n_counters cannot be assumed zero afterwards; the kernel resets its own.
-    ws.zeroed_counters = plan.n_counters;
     *out = ws.ptr;
     return GQA_OK;
 }
@@ -130,20 +141,23 @@ gqa_status gqa_decode_ex(const void *q, const void *k_cache, const void *v_cache
     if ((s = cu_count(device, &cus)) != GQA_OK)
         return s;
     gqa::DecodePlan plan;
-    if ((s = gqa::plan_decode(B, H, G, d_h, Tmax, dtype, split_tokens, cus, &plan, &err)) != GQA_OK)
+    if ((s = gqa::plan_decode(B, H, G, d_h, Tmax, dtype, split_tokens, cus, 0, &plan, &err)) != GQA_OK)
         return record(s, err);
-    if ((int64_t)G * plan.head_tiles > 65535)
+    if ((int64_t)(G / plan.gb) * plan.head_tiles > 65535)
         return record(GQA_ERR_UNSUPPORTED, "too many key/value heads");
 
-    gqa::DecodeArgs a{q, k_cache, v_cache, seqlens, B, H, G, d_h, Tmax, scale, out,
-                      nullptr, nullptr, nullptr, stream};
-    if (plan.splits > 1) {
+    gqa::DecodeArgs a{q, k_cache, v_cache, seqlens, B, H, G, d_h, Tmax, scale, out, nullptr, nullptr, stream};
+    if (dtype == GQA_BF16) {
+        int bpc = 0;
+        if ((s = blocks_per_cu(device, plan, d_h, &bpc)) != GQA_OK)
+            return s;
+        if ((s = gqa::plan_decode(B, H, G, d_h, Tmax, dtype, split_tokens, cus, bpc, &plan, &err)) != GQA_OK)
+            return record(s, err);
         char *ws = nullptr;
-        if ((s = workspace_for(device, stream, plan, &ws)) != GQA_OK)
+        if ((s = workspace_for(device, stream, plan.workspace_bytes, &ws)) != GQA_OK)
             return s;
         a.part = reinterpret_cast<float *>(ws + plan.part_offset);
         a.lse = reinterpret_cast<float *>(ws + plan.lse_offset);
-        a.counters = reinterpret_cast<int *>(ws + plan.counter_offset);
     }
     e = gqa::launch_decode(plan, a, dtype);
     if (e != hipSuccess)
@@ -195,13 +209,14 @@ gqa_status gqa_decode_plan(int B, int H, int G, int d_h, int Tmax, gqa_dtype dty
 {
     std::string err;
     gqa::DecodePlan plan;
-    gqa_status s = gqa::plan_decode(B, H, G, d_h, Tmax, dtype, split_tokens, cu_count, &plan, &err);
+    gqa_status s = gqa::plan_decode(B, H, G, d_h, Tmax, dtype, split_tokens, cu_count, 0, &plan, &err);
     if (s != GQA_OK)
         return record(s, err);
+    const bool fp32 = dtype == GQA_FP32 || B == 0;
     if (chunk_tokens)
-        *chunk_tokens = plan.chunk;
+        *chunk_tokens = fp32 ? Tmax : plan.full_P;
     if (num_splits)
-        *num_splits = plan.splits;
+        *num_splits = fp32 ? 1 : plan.nwg;
     if (workspace_bytes)
         *workspace_bytes = plan.workspace_bytes;
     return GQA_OK;

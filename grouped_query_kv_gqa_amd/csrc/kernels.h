@@ -13,13 +13,15 @@ struct DecodeArgs {
     int B, H, G, D, Tmax;
     float scale;
     void *out;
-    float *part;    // split partial rows, or null when the plan has one split
-    float *lse;     // split log-sum-exp values (base 2)
-    int *counters;  // per (sequence, group, head tile) arrival counters, zero between launches
+    float *part;  // partial rows (bf16 path)
+    float *lse;   // partial base-2 log-sum-exp values (bf16 path)
     hipStream_t stream;
 };
 
 hipError_t launch_decode(const DecodePlan &plan, const DecodeArgs &args, gqa_dtype dtype);
+
+// Workgroups of the plan's bf16 decode variant that fit on one compute unit.
+hipError_t decode_blocks_per_cu(const DecodePlan &plan, int d_h, int *blocks);
 
 struct PrefillArgs {
     const void *q, *k, *v;

@@ -3,6 +3,7 @@
 #include "plan.h"
 
 #include <cmath>
+#include <cstdlib>
 
 namespace gqa {
 
@@ -81,8 +82,15 @@ gqa_status check_decode(const void *q, const void *k, const void *v, const int32
     return GQA_OK;
 }
 
+int default_blocks_per_cu(int d_h, int nt)
+{
+    // gfx950 build: d_h = 64 with 32-head tiles runs two 4-wave workgroups per
+    // CU; every other variant is register-limited to one workgroup per CU.
+    return (d_h == 64 && nt == 2) ? 2 : 1;
+}
+
 gqa_status plan_decode(int B, int H, int G, int d_h, int Tmax, gqa_dtype dtype, int split_tokens,
-                       int cu_count, DecodePlan *plan, std::string *err)
+                       int cu_count, int blocks_per_cu, DecodePlan *plan, std::string *err)
 {
     if (B < 0 || Tmax < 0 || H < 1 || G < 1 || d_h < 1)
         return fail(err, GQA_ERR_INVALID_ARG, "bad sizes");
@@ -98,39 +106,60 @@ gqa_status plan_decode(int B, int H, int G, int d_h, int Tmax, gqa_dtype dtype, 
     p.r = H / G;
     p.nt = p.r <= 16 ? 1 : (p.r <= 32 ? 2 : 4);
     p.head_tiles = (int)ceil_div(p.r, 16 * p.nt);
-    if (dtype == GQA_FP32 || Tmax == 0 || B == 0) {
-        p.chunk = (int)round_up(Tmax > 0 ? Tmax : 1, kDecodeTile);
-        p.splits = 1;
-    } else {
-        int64_t chunk;
-        if (split_tokens > 0) {
-            chunk = round_up(split_tokens, kDecodeTile);
-        } else {
-            const int64_t cus = cu_count > 0 ? cu_count : 256;
-            const int64_t pairs = (int64_t)B * G * p.head_tiles;
-            const int64_t want = ceil_div(4 * cus, pairs);  // workgroups per (sequence, head tile)
-            chunk = round_up(ceil_div(Tmax, want), kDecodeTile);
-            if (chunk < kMinAutoChunk)
-                chunk = kMinAutoChunk;
+    // One 16-head tile per wave leaves room for 8-wave workgroups; wider tiles
+    // need the registers of 4-wave workgroups.
+    p.waves = p.nt == 1 ? 8 : 4;
+    p.gb = 1;
+    for (int c : {8, 4, 2}) {
+        if (c <= p.waves && G % c == 0) {
+            p.gb = c;
+            break;
         }
-        if (chunk > round_up(Tmax, kDecodeTile))
-            chunk = round_up(Tmax, kDecodeTile);
-        p.chunk = (int)chunk;
-        p.splits = (int)ceil_div(Tmax, chunk);
     }
-    if (p.splits > 1) {
-        const int64_t rows = (int64_t)B * H;
-        // counters first, then partial rows, then log-sum-exp values
-        int64_t off = 0;
-        p.counter_offset = off;
-        p.n_counters = (int64_t)B * G * p.head_tiles;
-        off = round_up(off + p.n_counters * 4, 256);
-        p.part_offset = off;
-        off = round_up(off + rows * p.splits * d_h * 4, 256);
-        p.lse_offset = off;
-        off = round_up(off + rows * p.splits * 4, 256);
-        p.workspace_bytes = off;
+    if (dtype == GQA_FP32 || B == 0) {
+        p.nwg = 0;
+        if (plan)
+            *plan = p;
+        return GQA_OK;
     }
+    const int64_t combos = (int64_t)(G / p.gb) * p.head_tiles;
+    const int64_t positions = (int64_t)B * Tmax;
+    const int64_t max_pieces = ceil_div(positions > 0 ? positions : 1, kDecodeTile);
+    int64_t nwg;
+    if (split_tokens > 0) {
+        p.fixed_P = (int)round_up(split_tokens, kDecodeTile);
+        nwg = ceil_div(positions > 0 ? positions : 1, p.fixed_P);
+        p.full_P = p.fixed_P;
+    } else {
+        const int64_t cus = cu_count > 0 ? cu_count : 256;
+        const int64_t bpc = blocks_per_cu > 0 ? blocks_per_cu : default_blocks_per_cu(d_h, p.nt);
+        nwg = (cus * bpc) / combos;
+        if (nwg < 1)
+            nwg = 1;
+        if (nwg > max_pieces)
+            nwg = max_pieces;
+        int64_t P = round_up(ceil_div(positions > 0 ? positions : 1, nwg), kDecodeTile);
+        p.full_P = (int)(P < kDecodeTile ? kDecodeTile : P);
+    }
+    if (nwg > 0x7fffffff)
+        return fail(err, GQA_ERR_UNSUPPORTED, "too many cache positions for the split size");
+    p.nwg = (int)nwg;
+    // Merge layout: enough slot lanes that each takes at most 4 pieces of a
+    // full-length row, the rest of the 64 lanes spread over d.
+    {
+        const int64_t exp_slots = (ceil_div(Tmax > 0 ? Tmax : 1, p.full_P) + 1) * (p.waves / p.gb);
+        int64_t ns = 1;
+        while (ns < 64 && ns * 4 < exp_slots)
+            ns *= 2;
+        const int64_t min_ns = 256 / d_h;  // at most d_h / 4 quads
+        if (ns < min_ns)
+            ns = min_ns;
+        p.merge_nq = (int)(64 / ns);
+    }
+    const int64_t slots = (nwg + B) * (int64_t)H * (p.waves / p.gb);
+    p.part_offset = 0;
+    p.lse_offset = round_up(slots * d_h * 4, 256);
+    p.workspace_bytes = round_up(p.lse_offset + slots * 4, 256);
     if (plan)
         *plan = p;
     return GQA_OK;

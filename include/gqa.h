@@ -73,10 +73,12 @@ typedef enum gqa_dtype { GQA_BF16 = 0, GQA_FP32 = 1 } gqa_dtype;
  *   out      [B, H, d_h]        same dtype as q
  *   out[b,h,:] = sum_t softmax_t(scale * q[b,h,:].k_cache[b,t,g(h),:]) v_cache[b,t,g(h),:]
  *
- * Long sequences are split over workgroups and the pieces are merged with a
- * log-sum-exp combine inside the same launch. The split workspace is owned by
- * the library, one per (device, stream), allocated on first use with
- * stream-ordered allocation and kept until the process ends.
+ * Work is balanced over the GPU by laying all sequences' cache positions
+ * end to end and giving every workgroup an equal slice; a sequence cut over
+ * several slices is merged with a log-sum-exp combine in a second launch on
+ * the same stream. The fp32 partial rows live in a library-owned workspace,
+ * one per (device, stream), allocated with stream-ordered allocation on first
+ * use, grown when needed, and kept until the process ends.
  * Requires 1 <= G, G divides H, Tmax >= 0, d_h in {64, 128}.
  */
 gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens,
@@ -84,10 +86,11 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, c
                       hipStream_t stream);
 
 /*
- * gqa_decode_ex -- gqa_decode with an explicit split size: each workgroup
- * takes at most `split_tokens` cache positions of one sequence (rounded up to
- * a multiple of 32). 0 selects the size gqa_decode would use. Results agree
- * with gqa_decode up to fp32 rounding of the combine. The fp32 path ignores
+ * gqa_decode_ex -- gqa_decode with an explicit slice length: every
+ * workgroup takes `split_tokens` consecutive positions (rounded up to a
+ * multiple of 32) of the end-to-end position space, instead of an equal share
+ * of it. 0 selects the equal share gqa_decode uses. Results agree with
+ * gqa_decode up to fp32 rounding of the combine. The fp32 path ignores
  * split_tokens. Same source passages as gqa_decode.
  */
 gqa_status gqa_decode_ex(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens,
@@ -130,13 +133,15 @@ gqa_status gqa_mean_pool_kv(const void *in, int64_t N, int H, int G, int d_h, gq
                             hipStream_t stream);
 
 /*
- * gqa_decode_plan -- the split plan gqa_decode_ex would use, computed on the
- * host without touching the GPU: `chunk_tokens` positions per workgroup,
- * `num_splits` = ceil(Tmax / chunk_tokens) workgroups per (sequence, group),
- * and the workspace bytes the split combine needs (0 when num_splits is 1).
- * `cu_count` is the GPU's compute-unit count (256 on MI355X). Any output
- * pointer may be NULL. Returns GQA_OK or the status gqa_decode would return
- * for the same sizes.
+ * gqa_decode_plan -- the bf16 decode partition gqa_decode_ex would use,
+ * computed on the host without touching the GPU (assuming the occupancy of
+ * the gfx950 build; the library itself asks the runtime): `num_splits`
+ * workgroups along the end-to-end position space, `chunk_tokens` positions
+ * per workgroup when every sequence holds Tmax positions (shorter sequences
+ * shrink the slice on the device), and the workspace bytes. For the fp32
+ * path: chunk_tokens = Tmax, num_splits = 1, workspace 0. `cu_count` is the
+ * GPU's compute-unit count (256 on MI355X). Any output pointer may be NULL.
+ * Returns GQA_OK or the status gqa_decode would return for the same sizes.
  */
 gqa_status gqa_decode_plan(int B, int H, int G, int d_h, int Tmax, gqa_dtype dtype, int split_tokens,
                            int cu_count, int *chunk_tokens, int *num_splits, int64_t *workspace_bytes);

@@ -83,20 +83,20 @@ def test_prefill_and_pool_argument_checks():
 
 
 def test_decode_plan():
-    # Llama-3-8B decode shape: 128 (sequence, group) pairs over 256 CUs
-    chunk, splits, ws = gq.decode_plan(16, 32, 8, 128, 4096)
-    assert chunk % 32 == 0 and splits == -(-4096 // chunk) and splits > 1 and ws > 0
-    # explicit split sizes round up to 32 positions
-    assert gq.decode_plan(2, 8, 2, 128, 1000, split_tokens=100)[:2] == (128, 8)
-    assert gq.decode_plan(2, 8, 2, 128, 1000, split_tokens=5000)[:2] == (1024, 1)
-    # one split needs no workspace; fp32 never splits
-    assert gq.decode_plan(2, 8, 2, 128, 1000, split_tokens=1000)[2] == 0
+    # Llama-3-8B decode shape: one 8-wave workgroup (8 groups) per CU, the
+    # 16 x 4096 positions cut into 256 slices of 256
+    chunk, nwg, ws = gq.decode_plan(16, 32, 8, 128, 4096)
+    assert (chunk, nwg) == (256, 256)
+    slots = (256 + 16) * 32
+    assert ws == slots * 128 * 4 + slots * 4
+    # explicit slice lengths round up to 32 positions
+    assert gq.decode_plan(2, 8, 2, 128, 1000, split_tokens=100)[:2] == (128, 16)
+    assert gq.decode_plan(2, 8, 2, 128, 1000, split_tokens=5000)[:2] == (5024, 1)
+    # one long sequence spread over every CU
+    assert gq.decode_plan(1, 64, 8, 128, 131072)[:2] == (512, 256)
+    # fp32 never splits
     import torch
     assert gq.decode_plan(1, 8, 2, 64, 256, dtype=torch.float32) == (256, 1, 0)
-    # workspace: counters + [B*H][splits][d_h] + [B*H][splits], 256-byte aligned
-    chunk, splits, ws = gq.decode_plan(1, 64, 8, 128, 131072, split_tokens=1024)
-    assert splits == 128
-    assert ws == 256 + 64 * 128 * 128 * 4 + 64 * 128 * 4
 
 
 def test_host_plan_sanitized(tmp_path):
@@ -110,15 +110,17 @@ int main() {
   std::string e; gqa::DecodePlan p;
   for (int B : {0, 1, 3, 64}) for (int H : {1, 8, 32, 64, 128}) for (int G = 1; G <= H; ++G) {
     if (H % G) continue;
-    for (int T : {0, 1, 31, 32, 33, 4096, 131072}) for (int s : {0, 32, 100, 1 << 20}) {
-      assert(gqa::plan_decode(B, H, G, 128, T, GQA_BF16, s, 256, &p, &e) == GQA_OK);
-      assert(p.splits >= 1 && p.chunk % 32 == 0 && (int64_t)p.chunk * p.splits >= T);
-      assert((int64_t)p.chunk * (p.splits - 1) < (T > 0 ? T : 1));
-      assert(p.head_tiles * 16 * p.nt >= H / G);
-      if (p.splits > 1) assert(p.workspace_bytes >= p.lse_offset + (int64_t)B * H * p.splits * 4);
+    for (int T : {0, 1, 31, 32, 33, 4096, 131072}) for (int s : {0, 32, 100, 1 << 20}) for (int bpc : {0, 1, 2}) {
+      assert(gqa::plan_decode(B, H, G, 128, T, GQA_BF16, s, 256, bpc, &p, &e) == GQA_OK);
+      assert(p.head_tiles * 16 * p.nt >= H / G && G % p.gb == 0 && p.waves % p.gb == 0);
+      if (B == 0) continue;
+      assert(p.nwg >= 1 && p.full_P >= 32 && p.full_P % 32 == 0);
+      assert((int64_t)p.full_P * p.nwg >= (int64_t)B * T);
+      assert(p.workspace_bytes >= p.lse_offset + ((int64_t)p.nwg + B) * H * (p.waves / p.gb) * 4);
+      assert(p.lse_offset >= ((int64_t)p.nwg + B) * H * (p.waves / p.gb) * 128 * 4);
     }
   }
-  assert(gqa::plan_decode(1, 6, 4, 128, 10, GQA_BF16, 0, 256, &p, &e) == GQA_ERR_INVALID_ARG);
+  assert(gqa::plan_decode(1, 6, 4, 128, 10, GQA_BF16, 0, 256, 0, &p, &e) == GQA_ERR_INVALID_ARG);
   char buf[64];
   assert(gqa::check_decode(buf, buf + 16, buf + 32, (const int32_t*)buf, 1, 8, 2, 128, 1, 1.f, GQA_BF16, buf, &e) == GQA_ERR_INVALID_ARG);
   std::puts("ok");
@@ -127,7 +129,7 @@ int main() {
 ''')
     exe = tmp_path / "t"
     csrc = os.path.join(ROOT, "grouped_query_kv_gqa_amd", "csrc")
-    subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+    subprocess.run(["g++", "-std=c++20", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
                     f"-I{csrc}", f"-I{os.path.join(ROOT, 'include')}", str(src), os.path.join(csrc, "plan.cpp"),
                     "-o", str(exe)], check=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
