@@ -25,6 +25,16 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// 32x32x16 bf16 MFMA, fp32 accumulate. Lane l supplies A[l%32][8*(l/32) .. +7]
+// and B[8*(l/32) .. +7][l%32]; register v = 4*m0 + m1 of the result holds
+// C[8*m0 + 4*(l/32) + m1][l%32].
+__device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes,
 // lane i addresses 4 consecutive 16-bit elements at row i/4, columns
 // 4*(i%4) .. +3 of a 4 x 16 block; after the read lane i holds column i of

@@ -6,8 +6,28 @@
 // implementation: broadcast of each key/value head to its H/G query heads,
 // scores over sqrt(d_h), causal mask, softmax over keys, times v).
 //
-// Row kernel: one wavefront per (b, t, h) row, lanes split d_h, online
-// softmax over the keys one position at a time, fp32 arithmetic.
+// bf16 MFMA kernel (flash-attention style, one pass over keys with an online
+// softmax; the score matrix never leaves registers):
+//  * Workgroup = (query tile, key/value group g, sequence b). Its 128 query
+//    rows are (token, head) pairs: QT = 128 / r consecutive tokens times the r
+//    heads of group g, so one K/V tile in LDS serves all heads of the group
+//    (the broadcast of the sketch costs no extra memory traffic).
+//  * 4 waves x 32 rows. Scores are computed transposed, S^T = K . Q^T, with
+//    32x32x16 bf16 MFMAs (keys in M, query rows in N): the result layout (a
+//    lane holds 16 keys of one row) is directly the B operand P^T of
+//    O^T = V^T . P^T, so P stays in registers.
+//  * K/V tiles of 64 positions are double-buffered in LDS: the next tile's
+//    global loads are in flight while the current one is used. K fragments
+//    are read with 16-byte LDS reads (rows padded by 16 bytes), V^T fragments
+//    with ds_read_b64_tr_b16 (rows padded by 32 bytes).
+//  * Causal: a query tile only visits key tiles up to its last token; the
+//    heaviest tiles are launched first.
+//  * Softmax statistics in base 2; the denominator sums the bf16-rounded
+//    probabilities that enter the P.V product.
+//
+// Row kernel (fp32 path, and groups of more than 128 query heads): one
+// wavefront per (b, t, h) row, lanes split d_h, online softmax over the keys
+// one position at a time, fp32 arithmetic.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -100,13 +120,213 @@ hipError_t launch_rows(const PrefillArgs &a)
     return hipGetLastError();
 }
 
+constexpr int kPfRows = 128;  // query rows (token, head) per workgroup
+constexpr int kPfBN = 64;     // key/value positions per tile
+
+template <int D>
+struct PfCfg {
+    static constexpr int KS = D / 16;                   // QK k-steps over d_h
+    static constexpr int DT = D / 32;                   // 32-wide d tiles of O^T
+    static constexpr int KSTRIDE = D + 8;               // K row stride (elements)
+    static constexpr int VSTRIDE = D + 16;              // V row stride (elements)
+    static constexpr int CH = D / 8;                    // 16-byte chunks per row
+    static constexpr int ROWS_PER_LOAD = 256 / CH;      // rows per cooperative load
+    static constexpr int LOADS = kPfBN / ROWS_PER_LOAD; // loads per tensor per thread
+    static constexpr int K_ELEMS = kPfBN * KSTRIDE;
+    static constexpr int V_ELEMS = kPfBN * VSTRIDE;
+};
+
+__device__ __forceinline__ u32x4_t ld16(const __bf16 *p)
+{
+    return *reinterpret_cast<const u32x4_t *>(p);
+}
+
+template <int D>
+__global__ void __launch_bounds__(256, 2)
+prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16 *vp, int T, int H, int G, int r,
+                    int QT, int causal, float scale_log2, __bf16 *__restrict__ out)
+{
+    using C = PfCfg<D>;
+    __shared__ __attribute__((aligned(16))) __bf16 Ks[2][C::K_ELEMS];
+    __shared__ __attribute__((aligned(16))) __bf16 Vs[2][C::V_ELEMS];
+
+    const int qt = gridDim.x - 1 - blockIdx.x;  // heaviest causal tiles first
+    const int g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, h = lane >> 5;
+    const int t0 = qt * QT;
+
+    // This lane's query row: column n of the wave's S^T tiles.
+    const int rho = wave * 32 + n;
+    const int tq = t0 + rho / r;
+    const int jh = rho % r;
+    const bool row_ok = rho < QT * r && tq < T;
+    const int64_t qrow = ((int64_t)b * T + min(tq, T - 1)) * H + g * r + jh;
+
+    // Q^T as the B operand: lane holds q[row][16*ks + 8*h .. +7].
+    bf16x8_t qf[C::KS];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+        u32x4_t x = {0, 0, 0, 0};
+        if (row_ok)
+            x = ld16(q + qrow * D + ks * 16 + h * 8);
+        qf[ks] = __builtin_bit_cast(bf16x8_t, x);
+    }
+
+    const int t_hi = min(T, t0 + QT);
+    const int kv_end = causal ? t_hi : T;
+    const int ntiles = (kv_end + kPfBN - 1) / kPfBN;
+
+    // Cooperative tile loads: thread -> (row tid/CH + ROWS_PER_LOAD*u, chunk tid%CH).
+    const int lrow = tid / C::CH, lch = tid % C::CH;
+    auto gload = [&](int tile, u32x4_t (&kr)[C::LOADS], u32x4_t (&vr)[C::LOADS]) {
+#pragma unroll
+        for (int u = 0; u < C::LOADS; ++u) {
+            const int t = min(tile * kPfBN + lrow + C::ROWS_PER_LOAD * u, T - 1);
+            const int64_t off = (((int64_t)b * T + t) * G + g) * D + lch * 8;
+            kr[u] = ld16(kp + off);
+            vr[u] = ld16(vp + off);
+        }
+    };
+    auto lstore = [&](int buf, int tile, const u32x4_t (&kr)[C::LOADS], const u32x4_t (&vr)[C::LOADS]) {
+#pragma unroll
+        for (int u = 0; u < C::LOADS; ++u) {
+            const int rl = lrow + C::ROWS_PER_LOAD * u;
+            const u32x4_t zero = {0, 0, 0, 0};
+            *reinterpret_cast<u32x4_t *>(&Ks[buf][rl * C::KSTRIDE + lch * 8]) = kr[u];
+            *reinterpret_cast<u32x4_t *>(&Vs[buf][rl * C::VSTRIDE + lch * 8]) =
+                (tile * kPfBN + rl < T) ? vr[u] : zero;
+        }
+    };
+
+    f32x16_t acc[C::DT];
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+        acc[dt] = (f32x16_t){};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    u32x4_t kr[C::LOADS], vr[C::LOADS];
+    gload(0, kr, vr);
+    lstore(0, 0, kr, vr);
+    for (int j = 0; j < ntiles; ++j) {
+        const int cur = j & 1;
+        const bool more = j + 1 < ntiles;
+        if (more)
+            gload(j + 1, kr, vr);  // in flight while tile j is used
+        __syncthreads();           // tile j visible; every wave is done with tile j-1
+
+        // S^T = K Q^T, two 32-key M tiles.
+        f32x16_t st[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            f32x16_t c = {};
+            const __bf16 *krow = &Ks[cur][(mt * 32 + n) * C::KSTRIDE + h * 8];
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks)
+                c = mfma32x32x16(__builtin_bit_cast(bf16x8_t, ld16(krow + ks * 16)), qf[ks], c);
+            st[mt] = c;
+        }
+
+        // Mask, scale (base 2) and online softmax. Register v of tile mt holds
+        // key j*64 + 32*mt + 8*(v/4) + 4*h + v%4 of row tq.
+        const int tk0 = j * kPfBN + 4 * h;
+        const int key_lim = causal ? tq : T - 1;  // last admissible key
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int tk = tk0 + 32 * mt + 8 * (v >> 2) + (v & 3);
+                const float x = (tk <= key_lim) ? st[mt][v] * scale_log2 : -INFINITY;
+                st[mt][v] = x;
+                mx = fmaxf(mx, x);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);
+        m_run = m_new;
+        bf16x8_t pf[2][2];
+        float psum = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int qh = 0; qh < 2; ++qh) {
+                f32x4_t a, c;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    a[i] = fast_exp2(st[mt][8 * qh + i] - m_use);
+                    c[i] = fast_exp2(st[mt][8 * qh + 4 + i] - m_use);
+                }
+                pf[mt][qh] = pack_bf16x8(a, c);
+                const u32x4_t pu = __builtin_bit_cast(u32x4_t, pf[mt][qh]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    psum += bf16_bits_to_f32(pu[i] & 0xffffu) + bf16_bits_to_f32(pu[i] >> 16);
+            }
+        l_run = l_run * alpha + psum;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+            acc[dt] *= alpha;
+
+        // O^T += V^T P^T: k-step (mt, qh) covers keys 32*mt + 16*qh + {4h..4h+3, 8+4h..8+4h+3}.
+        const int i16 = lane & 15, nh = n >> 4;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int qh = 0; qh < 2; ++qh) {
+                    const __bf16 *p0 = &Vs[cur][(32 * mt + 16 * qh + 4 * h + (i16 >> 2)) * C::VSTRIDE + dt * 32 +
+                                               16 * nh + 4 * (i16 & 3)];
+                    const bf16x4_t lo = lds_read_tr16(p0);
+                    const bf16x4_t hi = lds_read_tr16(p0 + 8 * C::VSTRIDE);
+                    acc[dt] = mfma32x32x16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf[mt][qh],
+                                           acc[dt]);
+                }
+
+        if (more)
+            lstore(cur ^ 1, j + 1, kr, vr);
+    }
+
+    // Epilogue: lane holds O^T[dt*32 + 8*m0 + 4*h + m1][row]; 4 consecutive d per (dt, m0).
+    l_run += __shfl_xor(l_run, 32, 64);
+    if (!row_ok)
+        return;
+    const float inv = 1.f / l_run;
+    __bf16 *dst = out + qrow * D + 4 * h;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int m0 = 0; m0 < 4; ++m0) {
+            u32x2_t u = {pack_bf16x2(acc[dt][4 * m0] * inv, acc[dt][4 * m0 + 1] * inv),
+                         pack_bf16x2(acc[dt][4 * m0 + 2] * inv, acc[dt][4 * m0 + 3] * inv)};
+            *reinterpret_cast<u32x2_t *>(dst + dt * 32 + 8 * m0) = u;
+        }
+}
+
+template <int D>
+hipError_t launch_mfma(const PrefillArgs &a)
+{
+    const int r = a.H / a.G;
+    const int QT = kPfRows / r;
+    const int nqt = (a.T + QT - 1) / QT;
+    const float scale_log2 = kLog2e / sqrtf((float)D);
+    prefill_bf16_kernel<D><<<dim3(nqt, a.G, a.B), 256, 0, a.stream>>>(
+        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), static_cast<const __bf16 *>(a.v), a.T,
+        a.H, a.G, r, QT, a.causal, scale_log2, static_cast<__bf16 *>(a.out));
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, gqa_dtype dtype)
 {
     if (dtype == GQA_FP32)
         return launch_rows<float>(a);
-    return launch_rows<__bf16>(a);
+    if (a.H / a.G > kPfRows)
+        return launch_rows<__bf16>(a);
+    return a.D == 64 ? launch_mfma<64>(a) : launch_mfma<128>(a);
 }
 
 }  // namespace gqa
