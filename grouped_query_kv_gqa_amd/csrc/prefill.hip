@@ -22,8 +22,9 @@
 //    with ds_read_b64_tr_b16 (rows padded by 32 bytes).
 //  * Causal: a query tile only visits key tiles up to its last token; the
 //    heaviest tiles are launched first.
-//  * Softmax statistics in base 2; the denominator sums the bf16-rounded
-//    probabilities that enter the P.V product.
+//  * Softmax in base 2 against a lazily moved per-row reference (rescaling
+//    only when a row maximum grows by more than 2^8); masking only on the
+//    tiles that cross the causal diagonal or the sequence end.
 //
 // Row kernel (fp32 path, and groups of more than 128 query heads): one
 // wavefront per (b, t, h) row, lanes split d_h, online softmax over the keys
@@ -161,6 +162,7 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     const int tq = t0 + rho / r;
     const int jh = rho % r;
     const bool row_ok = rho < QT * r && tq < T;
+    const int t_row_min = t0 + (wave * 32) / r;  // first query token of this wave
     const int64_t qrow = ((int64_t)b * T + min(tq, T - 1)) * H + g * r + jh;
 
     // Q^T as the B operand: lane holds q[row][16*ks + 8*h .. +7].
@@ -227,25 +229,45 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
             st[mt] = c;
         }
 
-        // Mask, scale (base 2) and online softmax. Register v of tile mt holds
-        // key j*64 + 32*mt + 8*(v/4) + 4*h + v%4 of row tq.
-        const int tk0 = j * kPfBN + 4 * h;
-        const int key_lim = causal ? tq : T - 1;  // last admissible key
+        // Online softmax in base 2 with a lazily moved reference m_run (in
+        // scaled units): p = 2^(s*c - m_run) with c = scale*log2(e). The
+        // reference only moves, rescaling O and l, when a row's maximum
+        // exceeds it by more than kLazy, so p <= 2^kLazy; softmax is
+        // unchanged by the choice of reference. Register v of tile mt holds
+        // key j*64 + 32*mt + 8*(v/4) + 4*h + v%4 of row tq. Only tiles that
+        // cross this wave's causal diagonal or the sequence end need masking.
+        constexpr float kLazy = 8.f;
+        const int tile_last = j * kPfBN + kPfBN - 1;
+        const bool need_mask = causal ? (tile_last > t_row_min) : (tile_last >= T);
+        if (need_mask) {
+            const int tk0 = j * kPfBN + 4 * h;
+            const int key_lim = causal ? tq : T - 1;  // last admissible key
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int tk = tk0 + 32 * mt + 8 * (v >> 2) + (v & 3);
+                    st[mt][v] = (tk <= key_lim) ? st[mt][v] : -INFINITY;
+                }
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int tk = tk0 + 32 * mt + 8 * (v >> 2) + (v & 3);
-                const float x = (tk <= key_lim) ? st[mt][v] * scale_log2 : -INFINITY;
-                st[mt][v] = x;
-                mx = fmaxf(mx, x);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        m_run = m_new;
+            for (int v = 0; v < 16; v += 2)
+                mx = fmaxf(mx, fmaxf(st[mt][v], st[mt][v + 1]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+        const bool move = mx > m_run + kLazy;
+        if (__any(move)) {
+            const float m_new = move ? mx : m_run;
+            const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt)
+                acc[dt] *= alpha;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         bf16x8_t pf[2][2];
         float psum = 0.f;
 #pragma unroll
@@ -255,19 +277,13 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
                 f32x4_t a, c;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    a[i] = fast_exp2(st[mt][8 * qh + i] - m_use);
-                    c[i] = fast_exp2(st[mt][8 * qh + 4 + i] - m_use);
+                    a[i] = fast_exp2(fmaf(st[mt][8 * qh + i], scale_log2, -m_use));
+                    c[i] = fast_exp2(fmaf(st[mt][8 * qh + 4 + i], scale_log2, -m_use));
+                    psum += a[i] + c[i];
                 }
                 pf[mt][qh] = pack_bf16x8(a, c);
-                const u32x4_t pu = __builtin_bit_cast(u32x4_t, pf[mt][qh]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    psum += bf16_bits_to_f32(pu[i] & 0xffffu) + bf16_bits_to_f32(pu[i] >> 16);
             }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt)
-            acc[dt] *= alpha;
+        l_run += psum;
 
         // O^T += V^T P^T: k-step (mt, qh) covers keys 32*mt + 16*qh + {4h..4h+3, 8+4h..8+4h+3}.
         const int i16 = lane & 15, nh = n >> 4;
