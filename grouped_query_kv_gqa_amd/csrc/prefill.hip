@@ -17,10 +17,16 @@
 //    lane holds 16 keys of one row) is directly the B operand P^T of
 //    O^T = V^T . P^T, so P stays in registers.
 //  * K/V tiles of 64 positions are double-buffered in LDS and loaded straight
-//    from global memory into LDS (global_load_lds_dwordx4, no staging
-//    registers); the next tile lands while the current one is used. Rows are
-//    unpadded with XOR-swizzled 16-byte chunks so that the 16-byte K reads and
-//    the V^T transposing reads (ds_read_b64_tr_b16) avoid bank conflicts.
+//    from global memory into LDS (buffer_load_dwordx4 ... lds, no staging
+//    registers; the buffer bounds turn rows past the sequence end into
+//    zeros). Rows are unpadded with XOR-swizzled 16-byte chunks so that the
+//    16-byte K reads and the V^T transposing reads (ds_read_b64_tr_b16) avoid
+//    bank conflicts.
+//  * Software pipeline over key tiles: while the matrix cores compute the
+//    scores of tile j+1, the vector ALUs turn the scores of tile j into
+//    probabilities; while they compute P_j V_j, the ALUs take the row maxima
+//    of tile j+1. K runs one tile ahead of V, so each load has a whole
+//    iteration to land.
 //  * Causal: a query tile only visits key tiles up to its last token; the
 //    heaviest tiles are launched first.
 //  * Softmax in base 2 against a lazily moved per-row reference (rescaling
@@ -30,6 +36,8 @@
 // Row kernel (fp32 path, and groups of more than 128 query heads): one
 // wavefront per (b, t, h) row, lanes split d_h, online softmax over the keys
 // one position at a time, fp32 arithmetic.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -122,21 +130,17 @@ hipError_t launch_rows(const PrefillArgs &a)
     return hipGetLastError();
 }
 
-constexpr int kPfBN = 64;  // key/value positions per tile
-#ifndef GQA_PREFILL_NTW
-#define GQA_PREFILL_NTW 1
-#endif
-constexpr int kPfNTW = GQA_PREFILL_NTW;  // 32-row column tiles per wave
+constexpr int kPfBN = 64;    // key/value positions per tile
+constexpr int kPfRows = 128; // query rows per workgroup: 4 waves x 32
 
-template <int D, int NTW>
+template <int D>
 struct PfCfg {
-    static constexpr int ROWS = 4 * 32 * NTW;           // query rows per workgroup (4 waves)
-    static constexpr int KS = D / 16;                   // QK k-steps over d_h
-    static constexpr int DT = D / 32;                   // 32-wide d tiles of O^T
-    static constexpr int CH = D / 8;                    // 16-byte chunks per row
-    static constexpr int WAVE_ROWS = 64 / CH;           // rows one wave load instruction fills
+    static constexpr int KS = D / 16;                     // QK k-steps over d_h
+    static constexpr int DT = D / 32;                     // 32-wide d tiles of O^T
+    static constexpr int CH = D / 8;                      // 16-byte chunks per row
+    static constexpr int WAVE_ROWS = 64 / CH;             // rows one wave load instruction fills
     static constexpr int LOADS = kPfBN / (4 * WAVE_ROWS); // load instructions per tensor per wave
-    static constexpr int TILE_ELEMS = kPfBN * D;        // unpadded rows, chunks swizzled
+    static constexpr int TILE_ELEMS = kPfBN * D;          // unpadded rows, chunks swizzled
 };
 
 // LDS tile layout: rows of d_h elements without padding; the 16-byte chunk c
@@ -155,18 +159,58 @@ __device__ __forceinline__ u32x4_t ld16(const __bf16 *p)
     return *reinterpret_cast<const u32x4_t *>(p);
 }
 
-// NTW = 32-row MFMA column tiles per wave: every K/V fragment read from LDS
-// feeds NTW independent MFMAs. With NTW = 2 a wave holds 64 query rows (its
-// accumulators live in AGPRs) and one 4-wave workgroup fills a compute unit.
-template <int D, int NTW>
-__global__ void __launch_bounds__(256, NTW == 1 ? 2 : 1)
+template <int I>
+using Ic = std::integral_constant<int, I>;
+
+// N buffer_load_dwordx4 ... lds from a raw buffer of nrec bytes at base:
+// instruction u reads byte voff + u*soff_step of the buffer (zeros past nrec)
+// into LDS at dst + u*dst_step elements, lane i at +16*i bytes.
+template <int N>
+__device__ __forceinline__ void buffer_rows_to_lds(const __bf16 *base, int nrec, __bf16 *dst, int dst_step, int voff,
+                                                   int soff_step)
+{
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16 *>(base), (short)0, nrec, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GQA_LDS void *)(dst + u * dst_step), 16, voff, u * soff_step,
+                                                 0, 0);
+}
+
+// Software pipeline over key tiles, one barrier per tile. Iteration j holds
+// the scores S_j of tile j in registers and, in one basic block, computes
+//   P_j = exp2(S_j * c - m)      (VALU)   while   S_{j+1} = K_{j+1} Q^T  (MFMA)
+//   O  += V_j^T P_j^T            (MFMA)   while   row max of S_{j+1}     (VALU)
+// so the matrix cores and the vector ALUs work on different tiles at once.
+// K is read one tile ahead of V, so the buffers are staggered: iteration j
+// reads K_{j+1} and V_j and loads K_{j+2} and V_{j+1} into the buffers that
+// held K_j and V_{j-1}.
+template <int D>
+__global__ void __launch_bounds__(256, 2)
 prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16 *vp, int T, int H, int G, int r,
                     int QT, int causal, float scale_log2, __bf16 *__restrict__ out)
 {
-    using C = PfCfg<D, NTW>;
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[2][C::TILE_ELEMS];
-    __shared__ __attribute__((aligned(16))) __bf16 Vs[2][C::TILE_ELEMS];
+    using C = PfCfg<D>;
     using SW = PfSwz<D>;
+    // Four separate LDS arrays (not one [2][...] array): the compiler then
+    // knows that reading one buffer does not touch another, so reads of the
+    // current tiles need not wait for the direct-to-LDS loads of the next.
+    __shared__ __attribute__((aligned(256))) __bf16 Ks0[C::TILE_ELEMS];
+    __shared__ __attribute__((aligned(256))) __bf16 Ks1[C::TILE_ELEMS];
+    __shared__ __attribute__((aligned(256))) __bf16 Vs0[C::TILE_ELEMS];
+    __shared__ __attribute__((aligned(256))) __bf16 Vs1[C::TILE_ELEMS];
+    auto kbuf = [&](auto i) -> __bf16 * {
+        if constexpr (decltype(i)::value == 0)
+            return Ks0;
+        else
+            return Ks1;
+    };
+    auto vbuf = [&](auto i) -> __bf16 * {
+        if constexpr (decltype(i)::value == 0)
+            return Vs0;
+        else
+            return Vs1;
+    };
 
     const int qt = gridDim.x - 1 - blockIdx.x;  // heaviest causal tiles first
     const int g = blockIdx.y, b = blockIdx.z;
@@ -174,240 +218,317 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     const int n = lane & 31, h = lane >> 5;
     const int t0 = qt * QT;
 
-    // This lane's query rows: column n of the wave's NTW S^T column tiles.
-    int tq[NTW];
-    bool row_ok[NTW];
-    int64_t qrow[NTW];
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-        const int rho = (wave * NTW + nt) * 32 + n;
-        tq[nt] = t0 + rho / r;
-        row_ok[nt] = rho < QT * r && tq[nt] < T;
-        qrow[nt] = ((int64_t)b * T + min(tq[nt], T - 1)) * H + g * r + rho % r;
-    }
-    const int t_row_min = t0 + (wave * NTW * 32) / r;  // first query token of this wave
+    // This lane's query row: column n of the wave's S^T column tile.
+    const int rho = wave * 32 + n;
+    const int tq = t0 + rho / r;
+    const bool row_ok = rho < QT * r && tq < T;
+    const int64_t qrow = ((int64_t)b * T + min(tq, T - 1)) * H + g * r + rho % r;
+    const int t_row_min = t0 + (wave * 32) / r;  // first query token of this wave
 
     // Q^T as the B operand: lane holds q[row][16*ks + 8*h .. +7].
-    bf16x8_t qf[NTW][C::KS];
+    bf16x8_t qf[C::KS];
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            u32x4_t x = {0, 0, 0, 0};
-            if (row_ok[nt])
-                x = ld16(q + qrow[nt] * D + ks * 16 + h * 8);
-            qf[nt][ks] = __builtin_bit_cast(bf16x8_t, x);
-        }
+    for (int ks = 0; ks < C::KS; ++ks) {
+        u32x4_t x = {0, 0, 0, 0};
+        if (row_ok)
+            x = ld16(q + qrow * D + ks * 16 + h * 8);
+        qf[ks] = __builtin_bit_cast(bf16x8_t, x);
+    }
 
     const int t_hi = min(T, t0 + QT);
     const int kv_end = causal ? t_hi : T;
     const int ntiles = (kv_end + kPfBN - 1) / kPfBN;
+    // Tiles below j_mask need no mask for any row of the workgroup.
+    const int j_mask = causal ? t0 / kPfBN : T / kPfBN;
 
     // Tile loads go straight from global memory into LDS
-    // (global_load_lds_dwordx4): lane i of a wave instruction fills the
+    // (buffer_load_dwordx4 ... lds): lane i of a wave instruction fills the
     // 16-byte LDS slot base + 16*i, i.e. row WAVE_ROWS*instr + i/CH, slot
     // i%CH, so it fetches the global chunk that the swizzle puts in that slot.
-    // Rows past the sequence end are clamped to its last row: their scores
-    // are masked to -inf, so they meet p = 0 with finite values.
-    const int srow = lane / C::CH, sslot = lane % C::CH;
-    auto tile_load = [&](int buf, int tile) {
+    // The buffer resource spans the tile's positions inside the sequence, so
+    // rows past the sequence end read as zeros (their scores are masked to
+    // -inf and their p is 0). The swizzle of a lane's rows does not depend on
+    // the instruction, so one per-lane offset serves all of them.
+    static_assert((4 * C::WAVE_ROWS) % C::CH == 0, "swizzle must repeat every instruction");
+    const int tok_bytes = G * D * 2;
+    const int rl0 = wave * C::WAVE_ROWS + lane / C::CH;  // tile row of this lane's first load
+    const int sslot = lane % C::CH;
+    const int voff_k = rl0 * tok_bytes + g * D * 2 + (sslot ^ SW::k(rl0)) * 16;
+    const int voff_v = rl0 * tok_bytes + g * D * 2 + (sslot ^ SW::v(rl0)) * 16;
+    auto load_tile = [&](const __bf16 *src, __bf16 *dst, int tile, bool is_v) {
+        const int row0 = tile * kPfBN;
+        const __bf16 *base = src + ((int64_t)b * T + row0) * G * D;
+        const int nrec = (min(T, row0 + kPfBN) - row0) * tok_bytes;
+        buffer_rows_to_lds<C::LOADS>(base, nrec, dst + wave * C::WAVE_ROWS * D, 4 * C::WAVE_ROWS * D,
+                                     is_v ? voff_v : voff_k, 4 * C::WAVE_ROWS * tok_bytes);
+    };
+
+    // LDS fragment addresses. The swizzles only permute chunks inside a
+    // row, and the chunk index splits into bits that vary per read and bits
+    // fixed per lane, so an address is a per-lane base XOR a constant
+    // (buffers are 256-byte aligned, rows 2*d_h bytes):
+    //  * K fragment (A operand of S^T = K Q^T) for k-step ks of M tile mt:
+    //    lane (n, h) reads chunk 2*ks + h of key row 32*mt + n, stored at slot
+    //    (2*ks) ^ (h ^ kswz(n)) (kswz(n + 32) = kswz(n)).
+    //  * V^T fragment (A operand of O^T = V^T P^T) for key k-step kstep and d
+    //    tile dt: keys 16*kstep + {4h..4h+3, 8+4h..8+4h+3}; lane reads row
+    //    16*kstep + 4*h + i16/4 (and 8 rows on), columns dt*32 + 16*nh +
+    //    4*(i16%4) .. +3, i.e. chunk 4*dt + x with x = 2*nh + (i16%4)/2, half
+    //    (i16%2), stored at slot (4*dt) ^ (x ^ vswz(row)) (vswz depends on
+    //    row % 4 only).
+    static_assert(D * 2 >= 128, "row must hold the XOR-ed bits");
+    const int i16 = lane & 15, nh = n >> 4;
+    const uint32_t kb_lane = n * D * 2 + ((h ^ SW::k(n)) * 16);
+    const int vrow = 4 * h + (i16 >> 2);
+    const uint32_t vb_lane =
+        vrow * D * 2 + (((2 * nh + ((i16 & 3) >> 1)) ^ SW::v(vrow)) * 16) + (i16 & 1) * 8;
+    auto kfrag = [&](const __bf16 *Kc, int ks, int mt) {
+        const char *a = (const char *)Kc + (kb_lane ^ (uint32_t)(32 * ks)) + mt * 32 * D * 2;
+        return __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)a);
+    };
+    auto vfrag = [&](const __bf16 *Vc, int kstep, int dt) {
+        const char *a = (const char *)Vc + (vb_lane ^ (uint32_t)(64 * dt)) + kstep * 16 * D * 2;
+        const bf16x4_t lo = lds_read_tr16((const __bf16 *)a);
+        const bf16x4_t hi = lds_read_tr16((const __bf16 *)(a + 8 * D * 2));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+
+    // S^T = K Q^T for one tile (prologue only): two 32-key M tiles.
+    auto qk = [&](const __bf16 *Kc, f32x16_t (&st)[2]) {
+        st[0] = st[1] = (f32x16_t){};
 #pragma unroll
-        for (int u = 0; u < C::LOADS; ++u) {
-            const int rl = (u * 4 + wave) * C::WAVE_ROWS + srow;  // tile row of this lane
-            const int t = min(tile * kPfBN + rl, T - 1);
-            const int64_t goff = (((int64_t)b * T + t) * G + g) * D;
-            const int lbase = (u * 4 + wave) * C::WAVE_ROWS * D;   // wave-uniform LDS base
-            __builtin_amdgcn_global_load_lds(
-                (__attribute__((address_space(1))) void *)(kp + goff + (sslot ^ SW::k(rl)) * 8),
-                (__attribute__((address_space(3))) void *)&Ks[buf][lbase], 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(
-                (__attribute__((address_space(1))) void *)(vp + goff + (sslot ^ SW::v(rl)) * 8),
-                (__attribute__((address_space(3))) void *)&Vs[buf][lbase], 16, 0, 0);
+        for (int ks = 0; ks < C::KS; ++ks) {
+            st[0] = mfma32x32x16(kfrag(Kc, ks, 0), qf[ks], st[0]);
+            st[1] = mfma32x32x16(kfrag(Kc, ks, 1), qf[ks], st[1]);
         }
     };
 
-    f32x16_t acc[NTW][C::DT];
-    float m_run[NTW], l_run[NTW];
+    // Register v of S^T tile mt holds key tile*64 + 32*mt + 8*(v/4) + 4*h + v%4.
+    auto mask = [&](f32x16_t (&st)[2], int tile) {
+        const int tile_last = tile * kPfBN + kPfBN - 1;
+        const bool need = causal ? (tile_last > t_row_min) : (tile_last >= T);
+        if (!need)
+            return;
+        const int key_lim = causal ? tq : T - 1;  // last admissible key
+        const int tk0 = tile * kPfBN + 4 * h;
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-        m_run[nt] = -INFINITY;
-        l_run[nt] = 0.f;
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt)
-            acc[nt][dt] = (f32x16_t){};
+            for (int v = 0; v < 16; ++v) {
+                const int tk = tk0 + 32 * mt + 8 * (v >> 2) + (v & 3);
+                st[mt][v] = (tk <= key_lim) ? st[mt][v] : -INFINITY;
+            }
+    };
+
+    // Online softmax in base 2 with a lazily moved reference m_run (in
+    // scaled units): p = 2^(s*c - m_run) with c = scale*log2(e). The
+    // reference only moves when a row maximum exceeds it by more than kLazy,
+    // so p <= 2^kLazy; softmax is unchanged by the choice of reference. A
+    // move found on tile j+1 rescales O and l at the start of the next
+    // iteration, after P_j V_j has been added.
+    constexpr float kLazy = 8.f;
+    float m_run = -INFINITY, l_run = 0.f, alpha = 1.f;
+    bool move = false;
+    // maximum() (NaN-propagating) maps to three-input v_maximum3 without the
+    // operand canonicalisation that fmaxf costs.
+    auto max_part = [&](const f32x16_t (&st)[2], int v, float &mx0, float &mx1) {
+        mx0 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx0, st[0][v]), st[0][v + 1]);
+        mx1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx1, st[1][v]), st[1][v + 1]);
+    };
+    auto max_finish = [&](float mx0, float mx1) {
+        float mx = __builtin_elementwise_maximum(mx0, mx1);
+        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+        move = mx > m_run + kLazy;
+        alpha = (move && m_run != -INFINITY) ? fast_exp2(m_run - mx) : (move ? 0.f : 1.f);
+        m_run = move ? mx : m_run;
+    };
+    auto row_max = [&](const f32x16_t (&st)[2]) {
+        float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; v += 2)
+            max_part(st, v, mx0, mx1);
+        max_finish(mx0, mx1);
+    };
+
+    // Chunk c (0..7) of P_j: p for the 4 scores st[mt][8*qh + 4*hf + i]
+    // (kk = c/2 = 2*mt + qh, hf = c%2), stored as bf16 pairs in words 2*hf,
+    // 2*hf + 1 of the P^T fragment pw[kk]. The row sum adds the bf16-rounded
+    // p that the P V product uses (dot product with (1, 1)).
+    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+    auto p_chunk = [&](const f32x16_t (&st)[2], int c, float m_use, u32x4_t (&pw)[4], float &ps0, float &ps1) {
+        const int kk = c >> 1, hf = c & 1, mt = kk >> 1, qh = kk & 1;
+        float e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            e[i] = fast_exp2(fmaf(st[mt][8 * qh + 4 * hf + i], scale_log2, -m_use));
+        const uint32_t w0 = pack_bf16x2(e[0], e[1]), w1 = pack_bf16x2(e[2], e[3]);
+        pw[kk][2 * hf] = w0;
+        pw[kk][2 * hf + 1] = w1;
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w0), ones, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w1), ones, ps1, false);
+    };
+
+    f32x16_t acc[C::DT];
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+        acc[dt] = (f32x16_t){};
+
+    auto rescale = [&]() {
+        l_run *= alpha;
+        if (__any(move)) {
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt)
+                acc[dt] *= alpha;
+        }
+    };
+
+    f32x16_t st[2][2];  // S_j lives in st[j % 2]
+
+    // Iteration j < ntiles - 1; P = j % 2 selects the buffers. The body is
+    // laid out by hand in steps fenced with sched_barrier: each QK step
+    // issues the K reads of the next step, two MFMAs and a chunk of the
+    // softmax of S_j; each P V step issues the V^T reads of the next step,
+    // one MFMA and part of the row maximum of S_{j+1}.
+    constexpr int kChunksPerStep = 8 / C::KS;
+    constexpr int kPvSteps = 4 * C::DT;
+    constexpr int kMaxStart = kPvSteps >= 12 ? 4 : 0;  // leave the last QK MFMAs time to finish
+    static_assert(kMaxStart + 8 <= kPvSteps, "row max takes 8 steps");
+    auto iter = [&](auto P, int j) {
+        constexpr int p = decltype(P)::value;
+        wait_vector_memory();  // this wave's loads of K_{j+1} and V_j have landed
+        __syncthreads();       // everyone's have; every wave is done with K_j and V_{j-1}
+        if (j + 2 < ntiles)
+            load_tile(kp, kbuf(Ic<p>{}), j + 2, false);
+        load_tile(vp, vbuf(Ic<1 - p>{}), j + 1, true);
+        rescale();
+        const __bf16 *Kc = kbuf(Ic<1 - p>{});
+        const __bf16 *Vc = vbuf(Ic<p>{});
+        f32x16_t(&sc)[2] = st[p];
+        f32x16_t(&sn)[2] = st[1 - p];
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        u32x4_t pw[4];
+        float ps0 = 0.f, ps1 = 0.f;
+        __builtin_amdgcn_sched_barrier(0);
+
+        bf16x8_t ka0 = kfrag(Kc, 0, 0), ka1 = kfrag(Kc, 0, 1);
+        sn[0] = sn[1] = (f32x16_t){};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            bf16x8_t kb0 = ka0, kb1 = ka1;
+            if (ks + 1 < C::KS) {
+                kb0 = kfrag(Kc, ks + 1, 0);
+                kb1 = kfrag(Kc, ks + 1, 1);
+            }
+            sn[0] = mfma32x32x16(ka0, qf[ks], sn[0]);
+            sn[1] = mfma32x32x16(ka1, qf[ks], sn[1]);
+#pragma unroll
+            for (int c = ks * kChunksPerStep; c < (ks + 1) * kChunksPerStep; ++c)
+                p_chunk(sc, c, m_use, pw, ps0, ps1);
+            __builtin_amdgcn_sched_barrier(0);
+            ka0 = kb0;
+            ka1 = kb1;
+        }
+        l_run += ps0 + ps1;
+
+        float mx0 = -INFINITY, mx1 = -INFINITY;
+        bf16x8_t va = vfrag(Vc, 0, 0);
+#pragma unroll
+        for (int s = 0; s < kPvSteps; ++s) {
+            const int kstep = s / C::DT, dt = s % C::DT;
+            bf16x8_t vb = va;
+            if (s + 1 < kPvSteps)
+                vb = vfrag(Vc, (s + 1) / C::DT, (s + 1) % C::DT);
+            acc[dt] = mfma32x32x16(va, __builtin_bit_cast(bf16x8_t, pw[kstep]), acc[dt]);
+            if (s >= kMaxStart && s < kMaxStart + 8)
+                max_part(sn, 2 * (s - kMaxStart), mx0, mx1);
+            __builtin_amdgcn_sched_barrier(0);
+            va = vb;
+        }
+        max_finish(mx0, mx1);
+    };
+    // Tail iterations (the tile after them needs a mask, or none follows):
+    // plain order, buffers picked at run time, S_j kept in st[0].
+    auto tail = [&](int j) {
+        const bool odd = j & 1;
+        wait_vector_memory();
+        __syncthreads();
+        const bool more = j + 1 < ntiles;
+        if (more) {
+            if (j + 2 < ntiles)
+                load_tile(kp, odd ? Ks1 : Ks0, j + 2, false);
+            load_tile(vp, odd ? Vs0 : Vs1, j + 1, true);
+        }
+        rescale();
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        u32x4_t pw[4];
+        float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            p_chunk(st[0], c, m_use, pw, ps0, ps1);
+        l_run += ps0 + ps1;
+        const __bf16 *Vc = odd ? Vs1 : Vs0;
+#pragma unroll
+        for (int s = 0; s < kPvSteps; ++s)
+            acc[s % C::DT] = mfma32x32x16(vfrag(Vc, s / C::DT, s % C::DT),
+                                          __builtin_bit_cast(bf16x8_t, pw[s / C::DT]), acc[s % C::DT]);
+        if (more) {
+            qk(odd ? Ks0 : Ks1, st[0]);
+            mask(st[0], j + 1);
+            row_max(st[0]);
+        }
+    };
+
+    // Prologue: K_0, V_0 and K_1 in flight, S_0 computed.
+    load_tile(kp, Ks0, 0, false);
+    load_tile(vp, Vs0, 0, true);
+    if (ntiles > 1)
+        load_tile(kp, Ks1, 1, false);
+    wait_vector_memory();
+    __syncthreads();
+    qk(Ks0, st[0]);
+    if (j_mask <= 0)
+        mask(st[0], 0);
+    row_max(st[0]);
+
+    const int n_fast = max(0, min(ntiles - 1, j_mask - 1));  // iterations whose next tile needs no mask
+    int j = 0;
+    for (; j + 1 < n_fast; j += 2) {
+        iter(Ic<0>{}, j);
+        iter(Ic<1>{}, j + 1);
     }
-
-    tile_load(0, 0);
-    for (int j = 0; j < ntiles; ++j) {
-        const int cur = j & 1;
-        wait_vector_memory();  // this wave's loads of tile j have landed in LDS
-        __syncthreads();       // everyone's have; every wave is done with tile j-1
-        if (j + 1 < ntiles)
-            tile_load(cur ^ 1, j + 1);  // lands while tile j is used
-
-        // S^T = K Q^T: two 32-key M tiles x NTW row tiles. Each K fragment
-        // (read from LDS one k-step ahead) feeds NTW independent MFMAs, and
-        // the M tiles alternate so consecutive MFMAs never share an
-        // accumulator.
-        f32x16_t st[NTW][2];
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt)
-            st[nt][0] = st[nt][1] = (f32x16_t){};
-        {
-            // lane (n, h) reads chunk 2*ks + h of rows n and 32 + n
-            const __bf16 *krow0 = &Ks[cur][n * D];
-            const __bf16 *krow1 = krow0 + 32 * D;
-            const int sw = SW::k(n);  // rows n and n + 32 share the swizzle
-            auto kfrag = [&](const __bf16 *row, int ks) {
-                return __builtin_bit_cast(bf16x8_t, ld16(row + ((2 * ks + h) ^ sw) * 8));
-            };
-            bf16x8_t ka0 = kfrag(krow0, 0);
-            bf16x8_t ka1 = kfrag(krow1, 0);
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) {
-                bf16x8_t kb0 = ka0, kb1 = ka1;
-                if (ks + 1 < C::KS) {
-                    kb0 = kfrag(krow0, ks + 1);
-                    kb1 = kfrag(krow1, ks + 1);
-                }
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) {
-                    st[nt][0] = mfma32x32x16(ka0, qf[nt][ks], st[nt][0]);
-                    st[nt][1] = mfma32x32x16(ka1, qf[nt][ks], st[nt][1]);
-                }
-                ka0 = kb0;
-                ka1 = kb1;
-            }
-        }
-
-        // Online softmax in base 2 with a lazily moved reference m_run (in
-        // scaled units): p = 2^(s*c - m_run) with c = scale*log2(e). The
-        // reference only moves, rescaling O and l, when a row's maximum
-        // exceeds it by more than kLazy, so p <= 2^kLazy; softmax is
-        // unchanged by the choice of reference. Register v of tile mt holds
-        // key j*64 + 32*mt + 8*(v/4) + 4*h + v%4. Only tiles that cross this
-        // wave's causal diagonal or the sequence end need masking.
-        constexpr float kLazy = 8.f;
-        const int tile_last = j * kPfBN + kPfBN - 1;
-        const bool need_mask = causal ? (tile_last > t_row_min) : (tile_last >= T);
-        if (need_mask) {
-            const int tk0 = j * kPfBN + 4 * h;
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                const int key_lim = causal ? tq[nt] : T - 1;  // last admissible key
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int tk = tk0 + 32 * mt + 8 * (v >> 2) + (v & 3);
-                        st[nt][mt][v] = (tk <= key_lim) ? st[nt][mt][v] : -INFINITY;
-                    }
-            }
-        }
-        bool move[NTW];
-        float m_old[NTW];
-        bool any_move = false;
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int v = 0; v < 16; v += 2)
-                    mx = fmaxf(mx, fmaxf(st[nt][mt][v], st[nt][mt][v + 1]));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
-            move[nt] = mx > m_run[nt] + kLazy;
-            m_old[nt] = m_run[nt];
-            m_run[nt] = move[nt] ? mx : m_run[nt];
-            any_move |= move[nt];
-        }
-        if (__any(any_move)) {
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                const float alpha = (m_old[nt] == -INFINITY) ? 0.f : fast_exp2(m_old[nt] - m_run[nt]);
-                l_run[nt] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < C::DT; ++dt)
-                    acc[nt][dt] *= alpha;
-            }
-        }
-        bf16x8_t pf[NTW][4];  // P^T for k-step (mt, qh) = 2*mt + qh
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-            const float m_use = (m_run[nt] == -INFINITY) ? 0.f : m_run[nt];
-            float psum = 0.f;
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int qh = 0; qh < 2; ++qh) {
-                    f32x4_t a, c;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        a[i] = fast_exp2(fmaf(st[nt][mt][8 * qh + i], scale_log2, -m_use));
-                        c[i] = fast_exp2(fmaf(st[nt][mt][8 * qh + 4 + i], scale_log2, -m_use));
-                        psum += a[i] + c[i];
-                    }
-                    pf[nt][2 * mt + qh] = pack_bf16x8(a, c);
-                }
-            l_run[nt] += psum;
-        }
-
-        // O^T += V^T P^T: k-step (mt, qh) covers keys 32*mt + 16*qh +
-        // {4h..4h+3, 8+4h..8+4h+3}. Each V^T fragment feeds NTW MFMAs with
-        // different accumulators.
-        const int i16 = lane & 15, nh = n >> 4;
-        // lane reads row 32*mt + 16*qh + 4*h + i16/4 (and 8 rows on), columns
-        // dt*32 + 16*nh + 4*(i16%4) .. +3: chunk 4*dt + 2*nh + (i16%4)/2, half (i16%2)
-        auto vfrag = [&](int kstep, int dt) {
-            const int mt = kstep >> 1, qh = kstep & 1;
-            const int row = 32 * mt + 16 * qh + 4 * h + (i16 >> 2);
-            const int chunk = 4 * dt + 2 * nh + ((i16 & 3) >> 1);
-            const int half = (i16 & 1) * 4;
-            const __bf16 *p0 = &Vs[cur][row * D + ((chunk ^ SW::v(row)) * 8) + half];
-            const __bf16 *p1 = &Vs[cur][(row + 8) * D + ((chunk ^ SW::v(row + 8)) * 8) + half];
-            const bf16x4_t lo = lds_read_tr16(p0);
-            const bf16x4_t hi = lds_read_tr16(p1);
-            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        };
-#pragma unroll
-        for (int kstep = 0; kstep < 4; ++kstep)
-#pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt) {
-                const bf16x8_t va = vfrag(kstep, dt);
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt)
-                    acc[nt][dt] = mfma32x32x16(va, pf[nt][kstep], acc[nt][dt]);
-            }
-
+    if (j < n_fast) {
+        iter(Ic<0>{}, j);
+        ++j;
+        st[0][0] = st[1][0];
+        st[0][1] = st[1][1];
     }
+    for (; j < ntiles; ++j)
+        tail(j);
 
     // Epilogue: lane holds O^T[dt*32 + 8*m0 + 4*h + m1][row]; 4 consecutive d per (dt, m0).
+    const float lsum = l_run + __shfl_xor(l_run, 32, 64);
+    if (!row_ok)
+        return;
+    const float inv = 1.f / lsum;
+    __bf16 *dst = out + qrow * D + 4 * h;
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-        const float lsum = l_run[nt] + __shfl_xor(l_run[nt], 32, 64);
-        if (!row_ok[nt])
-            continue;
-        const float inv = 1.f / lsum;
-        __bf16 *dst = out + qrow[nt] * D + 4 * h;
+    for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-            for (int m0 = 0; m0 < 4; ++m0) {
-                u32x2_t u = {pack_bf16x2(acc[nt][dt][4 * m0] * inv, acc[nt][dt][4 * m0 + 1] * inv),
-                             pack_bf16x2(acc[nt][dt][4 * m0 + 2] * inv, acc[nt][dt][4 * m0 + 3] * inv)};
-                *reinterpret_cast<u32x2_t *>(dst + dt * 32 + 8 * m0) = u;
-            }
-    }
+        for (int m0 = 0; m0 < 4; ++m0) {
+            u32x2_t u = {pack_bf16x2(acc[dt][4 * m0] * inv, acc[dt][4 * m0 + 1] * inv),
+                         pack_bf16x2(acc[dt][4 * m0 + 2] * inv, acc[dt][4 * m0 + 3] * inv)};
+            *reinterpret_cast<u32x2_t *>(dst + dt * 32 + 8 * m0) = u;
+        }
 }
 
-template <int D, int NTW>
+template <int D>
 hipError_t launch_mfma(const PrefillArgs &a)
 {
     const int r = a.H / a.G;
-    const int QT = PfCfg<D, NTW>::ROWS / r;
+    const int QT = kPfRows / r;
     const int nqt = (a.T + QT - 1) / QT;
     const float scale_log2 = kLog2e / sqrtf((float)D);
-    prefill_bf16_kernel<D, NTW><<<dim3(nqt, a.G, a.B), 256, 0, a.stream>>>(
+    prefill_bf16_kernel<D><<<dim3(nqt, a.G, a.B), 256, 0, a.stream>>>(
         static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), static_cast<const __bf16 *>(a.v), a.T,
         a.H, a.G, r, QT, a.causal, scale_log2, static_cast<__bf16 *>(a.out));
     return hipGetLastError();
@@ -419,9 +540,9 @@ hipError_t launch_prefill(const PrefillArgs &a, gqa_dtype dtype)
 {
     if (dtype == GQA_FP32)
         return launch_rows<float>(a);
-    if (a.H / a.G > PfCfg<128, kPfNTW>::ROWS)
+    if (a.H / a.G > kPfRows)
         return launch_rows<__bf16>(a);
-    return a.D == 64 ? launch_mfma<64, kPfNTW>(a) : launch_mfma<128, kPfNTW>(a);
+    return a.D == 64 ? launch_mfma<64>(a) : launch_mfma<128>(a);
 }
 
 }  // namespace gqa
