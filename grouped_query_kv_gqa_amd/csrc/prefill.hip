@@ -225,14 +225,22 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     const int64_t qrow = ((int64_t)b * T + min(tq, T - 1)) * H + g * r + rho % r;
     const int t_row_min = t0 + (wave * 32) / r;  // first query token of this wave
 
-    // Q^T as the B operand: lane holds q[row][16*ks + 8*h .. +7].
+    // Q^T as the B operand: lane holds q[row][16*ks + 8*h .. +7] times
+    // c = log2(e)/sqrt(d_h), rounded to bf16, so that the MFMA yields scores
+    // in base-2 units.
     bf16x8_t qf[C::KS];
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
         u32x4_t x = {0, 0, 0, 0};
         if (row_ok)
             x = ld16(q + qrow * D + ks * 16 + h * 8);
-        qf[ks] = __builtin_bit_cast(bf16x8_t, x);
+        f32x4_t lo, hi;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lo[i] = bf16_bits_to_f32(i & 1 ? x[i / 2] >> 16 : x[i / 2] & 0xffffu) * scale_log2;
+            hi[i] = bf16_bits_to_f32(i & 1 ? x[2 + i / 2] >> 16 : x[2 + i / 2] & 0xffffu) * scale_log2;
+        }
+        qf[ks] = pack_bf16x8(lo, hi);
     }
 
     const int t_hi = min(T, t0 + QT);
@@ -293,9 +301,10 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
 
-    // S^T = K Q^T for one tile (prologue only): two 32-key M tiles.
-    auto qk = [&](const __bf16 *Kc, f32x16_t (&st)[2]) {
-        st[0] = st[1] = (f32x16_t){};
+    // S^T = K Q^T - m for one tile (plain order): two 32-key M tiles, the
+    // accumulators starting at -m.
+    auto qk = [&](const __bf16 *Kc, f32x16_t (&st)[2], float m) {
+        st[0] = st[1] = (f32x16_t)(-m);
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
             st[0] = mfma32x32x16(kfrag(Kc, ks, 0), qf[ks], st[0]);
@@ -321,13 +330,15 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     };
 
     // Online softmax in base 2 with a lazily moved reference m_run (in
-    // scaled units): p = 2^(s*c - m_run) with c = scale*log2(e). The
-    // reference only moves when a row maximum exceeds it by more than kLazy,
-    // so p <= 2^kLazy; softmax is unchanged by the choice of reference. A
-    // move found on tile j+1 rescales O and l at the start of the next
+    // scaled units): p = 2^(s*c - m_run) with c = scale*log2(e). The score
+    // MFMAs start from -m_run, so registers hold x = s*c - m_run and p =
+    // 2^x. The reference only moves when a row maximum exceeds it by more
+    // than kLazy, so p <= 2^kLazy; softmax is unchanged by the choice of
+    // reference. A move by delta found on tile j+1 subtracts delta from its
+    // scores and rescales O and l by 2^-delta at the start of the next
     // iteration, after P_j V_j has been added.
     constexpr float kLazy = 8.f;
-    float m_run = -INFINITY, l_run = 0.f, alpha = 1.f;
+    float m_run = 0.f, l_run = 0.f, alpha = 1.f;
     bool move = false;
     // maximum() (NaN-propagating) maps to three-input v_maximum3 without the
     // operand canonicalisation that fmaxf costs.
@@ -335,12 +346,14 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         mx0 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx0, st[0][v]), st[0][v + 1]);
         mx1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx1, st[1][v]), st[1][v + 1]);
     };
+    float delta = 0.f;
     auto max_finish = [&](float mx0, float mx1) {
         float mx = __builtin_elementwise_maximum(mx0, mx1);
-        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
-        move = mx > m_run + kLazy;
-        alpha = (move && m_run != -INFINITY) ? fast_exp2(m_run - mx) : (move ? 0.f : 1.f);
-        m_run = move ? mx : m_run;
+        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32, 64));  // relative to m_run
+        move = mx > kLazy;
+        delta = move ? mx : 0.f;
+        alpha = fast_exp2(-delta);
+        m_run += delta;
     };
     auto row_max = [&](const f32x16_t (&st)[2]) {
         float mx0 = -INFINITY, mx1 = -INFINITY;
@@ -350,22 +363,19 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         max_finish(mx0, mx1);
     };
 
-    // Chunk c (0..7) of P_j: p for the 4 scores st[mt][8*qh + 4*hf + i]
-    // (kk = c/2 = 2*mt + qh, hf = c%2), stored as bf16 pairs in words 2*hf,
-    // 2*hf + 1 of the P^T fragment pw[kk]. The row sum adds the bf16-rounded
-    // p that the P V product uses (dot product with (1, 1)).
+    // The row sum adds the bf16-rounded p that the P V product uses (dot
+    // product with (1, 1)).
     const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
-    auto p_chunk = [&](const f32x16_t (&st)[2], int c, float m_use, u32x4_t (&pw)[4], float &ps0, float &ps1) {
-        const int kk = c >> 1, hf = c & 1, mt = kk >> 1, qh = kk & 1;
-        float e[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            e[i] = fast_exp2(fmaf(st[mt][8 * qh + 4 * hf + i], scale_log2, -m_use));
-        const uint32_t w0 = pack_bf16x2(e[0], e[1]), w1 = pack_bf16x2(e[2], e[3]);
-        pw[kk][2 * hf] = w0;
-        pw[kk][2 * hf + 1] = w1;
-        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w0), ones, ps0, false);
-        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w1), ones, ps1, false);
+    // Word w (0..15) of P_j: the bf16 pair for scores st[mt][8*qh + 2*i],
+    // +1 (kk = w/4 = 2*mt + qh, i = w%4), word i of pw[kk].
+    auto p_word = [&](const f32x16_t (&st)[2], int w, u32x4_t (&pw)[4], float &ps0, float &ps1) {
+        const int kk = w >> 2, i = w & 3, mt = kk >> 1, qh = kk & 1;
+        const float e0 = fast_exp2(st[mt][8 * qh + 2 * i]);
+        const float e1 = fast_exp2(st[mt][8 * qh + 2 * i + 1]);
+        const uint32_t x = pack_bf16x2(e0, e1);
+        pw[kk][i] = x;
+        float &ps = (w & 1) ? ps1 : ps0;
+        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x), ones, ps, false);
     };
 
     f32x16_t acc[C::DT];
@@ -373,12 +383,14 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     for (int dt = 0; dt < C::DT; ++dt)
         acc[dt] = (f32x16_t){};
 
-    auto rescale = [&]() {
-        l_run *= alpha;
+    auto rescale = [&](f32x16_t (&sc)[2]) {
         if (__any(move)) {
+            l_run *= alpha;
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt)
                 acc[dt] *= alpha;
+            sc[0] -= delta;
+            sc[1] -= delta;
         }
     };
 
@@ -389,9 +401,22 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     // issues the K reads of the next step, two MFMAs and a chunk of the
     // softmax of S_j; each P V step issues the V^T reads of the next step,
     // one MFMA and part of the row maximum of S_{j+1}.
-    constexpr int kChunksPerStep = 8 / C::KS;
+    constexpr int kPfDist = 2;  // LDS fragment reads run this many steps ahead
     constexpr int kPvSteps = 4 * C::DT;
-    constexpr int kMaxStart = kPvSteps >= 12 ? 4 : 0;  // leave the last QK MFMAs time to finish
+    // P_j words: the first kQkWords during the QK steps, the rest during the
+    // first P V steps, each before the step whose MFMA reads it; then the
+    // row max of S_{j+1} (8 steps), late enough for the last QK MFMAs.
+    constexpr bool kSplitP = D == 128;
+    constexpr int kQkWords = kSplitP ? 10 : 16;
+    constexpr auto qk_w0 = [](int ks) {  // first word computed in QK step ks
+        if constexpr (kSplitP)
+            return ks < 2 ? 2 * ks : ks + 2;
+        else
+            return ks * (16 / C::KS);
+    };
+    static_assert(qk_w0(C::KS) == kQkWords, "QK steps cover their words");
+    static_assert(16 - kQkWords <= 8 * C::DT, "late words precede their P V step");
+    constexpr int kMaxStart = kSplitP ? 16 - kQkWords : (kPvSteps >= 12 ? 4 : 0);
     static_assert(kMaxStart + 8 <= kPvSteps, "row max takes 8 steps");
     auto iter = [&](auto P, int j) {
         constexpr int p = decltype(P)::value;
@@ -400,50 +425,66 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         if (j + 2 < ntiles)
             load_tile(kp, kbuf(Ic<p>{}), j + 2, false);
         load_tile(vp, vbuf(Ic<1 - p>{}), j + 1, true);
-        rescale();
+        rescale(st[p]);
         const __bf16 *Kc = kbuf(Ic<1 - p>{});
         const __bf16 *Vc = vbuf(Ic<p>{});
         f32x16_t(&sc)[2] = st[p];
         f32x16_t(&sn)[2] = st[1 - p];
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         u32x4_t pw[4];
         float ps0 = 0.f, ps1 = 0.f;
         __builtin_amdgcn_sched_barrier(0);
 
-        bf16x8_t ka0 = kfrag(Kc, 0, 0), ka1 = kfrag(Kc, 0, 1);
-        sn[0] = sn[1] = (f32x16_t){};
+        // Fragments are read kPfDist steps ahead of their MFMA; inside a step
+        // the reads go first, then each MFMA followed by its share of VALU.
+        bf16x8_t kf[C::KS][2];
+#pragma unroll
+        for (int i = 0; i < kPfDist && i < C::KS; ++i) {
+            kf[i][0] = kfrag(Kc, i, 0);
+            kf[i][1] = kfrag(Kc, i, 1);
+        }
+        sn[0] = sn[1] = (f32x16_t)(-m_run);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-            bf16x8_t kb0 = ka0, kb1 = ka1;
-            if (ks + 1 < C::KS) {
-                kb0 = kfrag(Kc, ks + 1, 0);
-                kb1 = kfrag(Kc, ks + 1, 1);
+            if (ks + kPfDist < C::KS) {
+                kf[ks + kPfDist][0] = kfrag(Kc, ks + kPfDist, 0);
+                kf[ks + kPfDist][1] = kfrag(Kc, ks + kPfDist, 1);
             }
-            sn[0] = mfma32x32x16(ka0, qf[ks], sn[0]);
-            sn[1] = mfma32x32x16(ka1, qf[ks], sn[1]);
+            sn[0] = mfma32x32x16(kf[ks][0], qf[ks], sn[0]);
+            sn[1] = mfma32x32x16(kf[ks][1], qf[ks], sn[1]);
 #pragma unroll
-            for (int c = ks * kChunksPerStep; c < (ks + 1) * kChunksPerStep; ++c)
-                p_chunk(sc, c, m_use, pw, ps0, ps1);
+            for (int w = qk_w0(ks); w < qk_w0(ks + 1); ++w)
+                p_word(sc, w, pw, ps0, ps1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x402, 48 / C::KS, 0);  // VALU incl. transcendental
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x402, 48 / C::KS, 0);
             __builtin_amdgcn_sched_barrier(0);
-            ka0 = kb0;
-            ka1 = kb1;
         }
-        l_run += ps0 + ps1;
 
         float mx0 = -INFINITY, mx1 = -INFINITY;
-        bf16x8_t va = vfrag(Vc, 0, 0);
+        bf16x8_t vf[kPvSteps];
+#pragma unroll
+        for (int i = 0; i < kPfDist; ++i)
+            vf[i] = vfrag(Vc, i / C::DT, i % C::DT);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < kPvSteps; ++s) {
             const int kstep = s / C::DT, dt = s % C::DT;
-            bf16x8_t vb = va;
-            if (s + 1 < kPvSteps)
-                vb = vfrag(Vc, (s + 1) / C::DT, (s + 1) % C::DT);
-            acc[dt] = mfma32x32x16(va, __builtin_bit_cast(bf16x8_t, pw[kstep]), acc[dt]);
+            if (s + kPfDist < kPvSteps)
+                vf[s + kPfDist] = vfrag(Vc, (s + kPfDist) / C::DT, (s + kPfDist) % C::DT);
+            acc[dt] = mfma32x32x16(vf[s], __builtin_bit_cast(bf16x8_t, pw[kstep]), acc[dt]);
+            if (s < 16 - kQkWords)
+                p_word(sc, kQkWords + s, pw, ps0, ps1);
             if (s >= kMaxStart && s < kMaxStart + 8)
                 max_part(sn, 2 * (s - kMaxStart), mx0, mx1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
             __builtin_amdgcn_sched_barrier(0);
-            va = vb;
         }
+        l_run += ps0 + ps1;
         max_finish(mx0, mx1);
     };
     // Tail iterations (the tile after them needs a mask, or none follows):
@@ -458,13 +499,12 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
                 load_tile(kp, odd ? Ks1 : Ks0, j + 2, false);
             load_tile(vp, odd ? Vs0 : Vs1, j + 1, true);
         }
-        rescale();
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        rescale(st[0]);
         u32x4_t pw[4];
         float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-            p_chunk(st[0], c, m_use, pw, ps0, ps1);
+        for (int w = 0; w < 16; ++w)
+            p_word(st[0], w, pw, ps0, ps1);
         l_run += ps0 + ps1;
         const __bf16 *Vc = odd ? Vs1 : Vs0;
 #pragma unroll
@@ -472,7 +512,7 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
             acc[s % C::DT] = mfma32x32x16(vfrag(Vc, s / C::DT, s % C::DT),
                                           __builtin_bit_cast(bf16x8_t, pw[s / C::DT]), acc[s % C::DT]);
         if (more) {
-            qk(odd ? Ks0 : Ks1, st[0]);
+            qk(odd ? Ks0 : Ks1, st[0], m_run);
             mask(st[0], j + 1);
             row_max(st[0]);
         }
@@ -485,10 +525,22 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         load_tile(kp, Ks1, 1, false);
     wait_vector_memory();
     __syncthreads();
-    qk(Ks0, st[0]);
+    qk(Ks0, st[0], 0.f);
     if (j_mask <= 0)
         mask(st[0], 0);
-    row_max(st[0]);
+    {
+        // The first reference is the row maximum of tile 0 (which holds at
+        // least one admissible key of every row).
+        float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; v += 2)
+            max_part(st[0], v, mx0, mx1);
+        float mx = __builtin_elementwise_maximum(mx0, mx1);
+        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32, 64));
+        m_run = (mx == -INFINITY) ? 0.f : mx;
+        st[0][0] -= m_run;
+        st[0][1] -= m_run;
+    }
 
     const int n_fast = max(0, min(ntiles - 1, j_mask - 1));  // iterations whose next tile needs no mask
     int j = 0;
