@@ -247,7 +247,9 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "G": w.G, "d_h": w.D, "context": w.Tmax,
                    "seed": args.seed, "input_copies": 4, "split_plan": list(dec["plan"][:2])},
         "roofline": {
-            "kernel": "decode_bf16_kernel",
+            # one gqa_decode call = the split kernel + the merge kernel; the
+            # HIP events bracket both (and the gap between them)
+            "kernel": "decode_bf16_kernel+decode_merge_kernel",
             "bound": "hbm",
             "achieved": round(kernel_gbs, 2),
             "peak": HBM_PEAK_GBS,
@@ -268,7 +270,7 @@ def main():
             "value": round(pf["flops"] * args.prefill_steps / pf["wall"] / 1e12, 3), "unit": "TFLOP/s",
             "steps": args.prefill_steps, "warmup": args.prefill_warmup,
             "ms_per_step": round(pf["wall"] / args.prefill_steps * 1e3, 4),
-            "roofline": {"kernel": "prefill", "bound": "mfma", "achieved": round(tflops, 3),
+            "roofline": {"kernel": "prefill_bf16_kernel", "bound": "mfma", "achieved": round(tflops, 3),
                          "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 5),
                          "traffic": measured_traffic("prefill"), "flops_per_launch": pf["flops"],
