@@ -384,27 +384,22 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
     constexpr int DCH = 4 * NQ;      // d values per item
     constexpr int NDC = D / DCH;     // items per row
     constexpr int NS = 64 / NQ;      // slot lanes
-    __shared__ int64_t s_red[2][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.y;
+    const int item = blockIdx.x * 4 + wave;
+    if (item >= H * NDC)
+        return;
 
-    // partition and this sequence's first flat position, once per workgroup
+    // partition and this sequence's first flat position (each wave on its own)
     int64_t tot = 0, pre = 0;
-    for (int i = tid; i < B; i += 256) {
+    for (int i = lane; i < B; i += 64) {
         const int Li = clamp_len(seqlens[i], Tmax);
         tot += Li;
         if (i < b)
             pre += Li;
     }
     tot = wave_sum_i64(tot);
-    pre = wave_sum_i64(pre);
-    if (lane == 0) {
-        s_red[0][wave] = tot;
-        s_red[1][wave] = pre;
-    }
-    __syncthreads();
-    tot = s_red[0][0] + s_red[0][1] + s_red[0][2] + s_red[0][3];
-    const int64_t pre_b = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
+    const int64_t pre_b = wave_sum_i64(pre);
     int64_t P;
     if (fixed_P > 0) {
         P = fixed_P;
@@ -415,9 +410,6 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
             P = kTile;
     }
 
-    const int item = blockIdx.x * 4 + wave;
-    if (item >= H * NDC)
-        return;
     const int h = item / NDC, dc = item % NDC;
     const int sl = lane / NQ, qd = lane % NQ;
     const int d0 = dc * DCH + qd * 4;
