@@ -131,7 +131,8 @@ hipError_t launch_rows(const PrefillArgs &a)
 }
 
 constexpr int kPfBN = 64;    // key/value positions per tile
-constexpr int kPfRows = 128; // query rows per workgroup: 4 waves x 32
+constexpr int kPfWaves = 4;             // waves per workgroup, 32 query rows each
+constexpr int kPfRows = 32 * kPfWaves;  // query rows per workgroup
 
 template <int D>
 struct PfCfg {
@@ -139,7 +140,7 @@ struct PfCfg {
     static constexpr int DT = D / 32;                     // 32-wide d tiles of O^T
     static constexpr int CH = D / 8;                      // 16-byte chunks per row
     static constexpr int WAVE_ROWS = 64 / CH;             // rows one wave load instruction fills
-    static constexpr int LOADS = kPfBN / (4 * WAVE_ROWS); // load instructions per tensor per wave
+    static constexpr int LOADS = kPfBN / (kPfWaves * WAVE_ROWS); // load instructions per tensor per wave
     static constexpr int TILE_ELEMS = kPfBN * D;          // unpadded rows, chunks swizzled
 };
 
@@ -186,7 +187,7 @@ __device__ __forceinline__ void buffer_rows_to_lds(const __bf16 *base, int nrec,
 // reads K_{j+1} and V_j and loads K_{j+2} and V_{j+1} into the buffers that
 // held K_j and V_{j-1}.
 template <int D>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(64 * kPfWaves, 8 / kPfWaves)
 prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16 *vp, int T, int H, int G, int r,
                     int QT, int causal, float scale_log2, __bf16 *__restrict__ out)
 {
@@ -257,7 +258,7 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     // rows past the sequence end read as zeros (their scores are masked to
     // -inf and their p is 0). The swizzle of a lane's rows does not depend on
     // the instruction, so one per-lane offset serves all of them.
-    static_assert((4 * C::WAVE_ROWS) % C::CH == 0, "swizzle must repeat every instruction");
+    static_assert((kPfWaves * C::WAVE_ROWS) % C::CH == 0, "swizzle must repeat every instruction");
     const int tok_bytes = G * D * 2;
     const int rl0 = wave * C::WAVE_ROWS + lane / C::CH;  // tile row of this lane's first load
     const int sslot = lane % C::CH;
@@ -267,8 +268,8 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         const int row0 = tile * kPfBN;
         const __bf16 *base = src + ((int64_t)b * T + row0) * G * D;
         const int nrec = (min(T, row0 + kPfBN) - row0) * tok_bytes;
-        buffer_rows_to_lds<C::LOADS>(base, nrec, dst + wave * C::WAVE_ROWS * D, 4 * C::WAVE_ROWS * D,
-                                     is_v ? voff_v : voff_k, 4 * C::WAVE_ROWS * tok_bytes);
+        buffer_rows_to_lds<C::LOADS>(base, nrec, dst + wave * C::WAVE_ROWS * D, kPfWaves * C::WAVE_ROWS * D,
+                                     is_v ? voff_v : voff_k, kPfWaves * C::WAVE_ROWS * tok_bytes);
     };
 
     // LDS fragment addresses. The swizzles only permute chunks inside a
@@ -580,7 +581,7 @@ hipError_t launch_mfma(const PrefillArgs &a)
     const int QT = kPfRows / r;
     const int nqt = (a.T + QT - 1) / QT;
     const float scale_log2 = kLog2e / sqrtf((float)D);
-    prefill_bf16_kernel<D><<<dim3(nqt, a.G, a.B), 256, 0, a.stream>>>(
+    prefill_bf16_kernel<D><<<dim3(nqt, a.G, a.B), 64 * kPfWaves, 0, a.stream>>>(
         static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), static_cast<const __bf16 *>(a.v), a.T,
         a.H, a.G, r, QT, a.causal, scale_log2, static_cast<__bf16 *>(a.out));
     return hipGetLastError();
