@@ -27,7 +27,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gqa_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-BF16, F32, F64 = 0, 1, 2
+BF16, F32, F64, F16 = 0, 1, 2, 3
 
 _lib = None
 
@@ -54,6 +54,14 @@ def _declare(lib):
     lib.oracle_prefill.restype = None
     lib.oracle_mean_pool.argtypes = [c_void_p, c_int, c_int64, c_int, c_int, c_int, c_void_p]
     lib.oracle_mean_pool.restype = None
+    lib.oracle_decode_step.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_int,
+                                       c_int, c_int, c_int, c_int, c_double, c_int, c_void_p]
+    lib.oracle_decode_step.restype = None
+    lib.oracle_prefill_window.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
+                                          c_int, c_int, c_void_p, c_void_p, c_void_p, c_int64, c_void_p]
+    lib.oracle_prefill_window.restype = None
+    lib.oracle_weighted_pool.argtypes = [c_void_p, c_int, c_int64, c_int, c_int, c_int, c_void_p, c_void_p]
+    lib.oracle_weighted_pool.restype = None
     lib.oracle_set_threads.argtypes = [c_int]
     lib.oracle_set_threads.restype = None
     lib.oracle_max_threads.argtypes = []
@@ -85,12 +93,16 @@ def _as_array(x):
                 raise ValueError("oracle inputs must be CPU tensors")
             if x.dtype == torch.bfloat16:
                 return np.ascontiguousarray(x.contiguous().view(torch.int16).numpy().view(np.uint16)), BF16
+            if x.dtype == torch.float16:
+                return np.ascontiguousarray(x.contiguous().view(torch.int16).numpy().view(np.uint16)), F16
             x = x.contiguous().numpy()
     except ImportError:
         pass
     x = np.ascontiguousarray(x)
     if x.dtype == np.uint16:
         return x, BF16
+    if x.dtype == np.float16:
+        return x.view(np.uint16), F16
     if x.dtype == np.float32:
         return x, F32
     if x.dtype == np.float64:
@@ -156,6 +168,75 @@ def prefill(q, k, v, causal: bool = True, rows=None, lib=None):
     out = np.empty((n, D), dtype=np.float64)
     lib.oracle_prefill(_ptr(qa), _ptr(ka), _ptr(va), dtype, B, T, H, G, D, int(bool(causal)),
                        _ptr(rb), _ptr(rt), _ptr(rh), n, _ptr(out))
+    return out
+
+
+def _seqlens(seqlens, B):
+    sl = np.ascontiguousarray(np.asarray(seqlens if not hasattr(seqlens, "numpy") else seqlens.numpy(),
+                                         dtype=np.int32))
+    assert sl.shape == (B,)
+    return sl
+
+
+def decode_step(q, k_cache, v_cache, seqlens, scale: float, k_new=None, v_new=None, window: int = 0, lib=None):
+    """Decode with an optional cache append (k_new, v_new [B,G,D]) and an
+    optional sliding window. Returns (out [B,H,D] fp64, k_after, v_after):
+    the caches after the append, as arrays of the stored bits (the inputs are
+    not modified)."""
+    lib = lib or load()
+    qa, ka, va = _as_array(q), _as_array(k_cache), _as_array(v_cache)
+    arrs = [qa, ka, va]
+    if k_new is not None:
+        kn, vn = _as_array(k_new), _as_array(v_new)
+        arrs += [kn, vn]
+    dtype = _same_kind(*arrs)
+    qa = qa[0]
+    ka, va = ka[0].copy(), va[0].copy()
+    B, H, D = qa.shape
+    Bk, Tmax, G, Dk = ka.shape
+    assert (Bk, Dk) == (B, D) and va.shape == ka.shape
+    kp = vp = None
+    if k_new is not None:
+        kn, vn = kn[0], vn[0]
+        assert kn.shape == (B, G, D) and vn.shape == (B, G, D)
+        kp, vp = _ptr(kn), _ptr(vn)
+    sl = _seqlens(seqlens, B)
+    out = np.empty((B, H, D), dtype=np.float64)
+    lib.oracle_decode_step(_ptr(qa), kp, vp, _ptr(ka), _ptr(va), dtype, _ptr(sl), B, H, G, D, Tmax, float(scale),
+                           int(window), _ptr(out))
+    return out, ka, va
+
+
+def prefill_window(q, k, v, window: int, rows=None, lib=None):
+    """Causal prefill where query t sees keys [max(0, t+1-window), t]."""
+    lib = lib or load()
+    qa, ka, va = _as_array(q), _as_array(k), _as_array(v)
+    dtype = _same_kind(qa, ka, va)
+    qa, ka, va = qa[0], ka[0], va[0]
+    B, T, H, D = qa.shape
+    G = ka.shape[2]
+    assert ka.shape == (B, T, G, D) and va.shape == ka.shape
+    if rows is None:
+        out = np.empty((B, T, H, D), dtype=np.float64)
+        lib.oracle_prefill_window(_ptr(qa), _ptr(ka), _ptr(va), dtype, B, T, H, G, D, int(window),
+                                  None, None, None, 0, _ptr(out))
+        return out
+    rb, rt, rh = (np.ascontiguousarray(np.asarray(a, dtype=np.int32)) for a in rows)
+    out = np.empty((rb.shape[0], D), dtype=np.float64)
+    lib.oracle_prefill_window(_ptr(qa), _ptr(ka), _ptr(va), dtype, B, T, H, G, D, int(window),
+                              _ptr(rb), _ptr(rt), _ptr(rh), rb.shape[0], _ptr(out))
+    return out
+
+
+def weighted_pool(x, G: int, w, lib=None):
+    """x [N,H,D], w [H] -> [N,G,D]: group g = sum of w[i] x[:, i, :] over its heads."""
+    lib = lib or load()
+    xa, dtype = _as_array(x)
+    N, H, D = xa.shape
+    wa = np.ascontiguousarray(np.asarray(w.numpy() if hasattr(w, "numpy") else w, dtype=np.float64))
+    assert wa.shape == (H,)
+    out = np.empty((N, G, D), dtype=np.float64)
+    lib.oracle_weighted_pool(_ptr(xa), dtype, N, H, G, D, _ptr(wa), _ptr(out))
     return out
 
 

@@ -30,7 +30,12 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_BF16 = 0, ORACLE_F32 = 1, ORACLE_F64 = 2 };
+enum { ORACLE_BF16 = 0, ORACLE_F32 = 1, ORACLE_F64 = 2, ORACLE_F16 = 3 };
+
+static size_t elem_bytes(int dtype)
+{
+    return dtype == ORACLE_F64 ? 8 : (dtype == ORACLE_F32 ? 4 : 2);
+}
 
 /* Exact widening of one stored element to double. A bf16 value is the upper
  * half of an IEEE binary32, so shifting its 16 bits up gives the same number
@@ -42,6 +47,20 @@ static double widen(const void *base, int64_t i, int dtype)
         float f;
         memcpy(&f, &u, sizeof f);
         return (double)f;
+    }
+    if (dtype == ORACLE_F16) {
+        /* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
+         * bits. Normal: (1024 + frac) * 2^(exp - 25); subnormal: frac * 2^-24. */
+        uint16_t hbits = ((const uint16_t *)base)[i];
+        int sign = hbits >> 15, ex = (hbits >> 10) & 31, frac = hbits & 1023;
+        double mag;
+        if (ex == 0)
+            mag = ldexp((double)frac, -24);
+        else if (ex == 31)
+            mag = frac ? NAN : INFINITY;
+        else
+            mag = ldexp((double)(frac + 1024), ex - 25);
+        return sign ? -mag : mag;
     }
     if (dtype == ORACLE_F32)
         return (double)((const float *)base)[i];
@@ -188,6 +207,120 @@ void oracle_prefill(const void *q, const void *k, const void *v, int dtype, int 
         int64_t q_off = (((int64_t)b * T + t) * H + h) * D;
         int64_t key_base = ((int64_t)b * T * G + g) * D;
         attend_row(q, q_off, k, v, key_base, (int64_t)G * D, L, D, dtype, scale, out + row * D, NULL);
+    }
+}
+
+/* Decode with the two common variants of a serving step, each optional:
+ *
+ *  Cache append (k_new, v_new not NULL). The new token's key and value join
+ *  the cache before it is read: [KB] section 1, a decode step reads every
+ *  cached entry, the new one included; section 2, Setup, head i attends over
+ *  the keys and values cached so far. With L_b = clamp(seqlens[b], 0, Tmax):
+ *  if L_b < Tmax, k_new[b] and v_new[b] ([G, D], every group) are written to
+ *  cache position L_b and the sequence then holds L_b + 1 positions; a full
+ *  cache (L_b = Tmax) is left unchanged and holds Tmax positions. k and v are
+ *  updated in place.
+ *
+ *  Sliding window (window > 0): each query attends only to the `window` most
+ *  recent positions of its sequence, [max(0, L - window), L) ([KB] section 4,
+ *  Empirical evidence, Mistral 7B ablation: GQA-8 combined with
+ *  sliding-window attention; the page gives no formula, and "the window most
+ *  recent positions, the newest included" is the reading taken here).
+ *  window = 0 keeps every position.
+ *
+ *   q            [B, H, D];  k_new, v_new [B, G, D] or NULL
+ *   k, v         [B, Tmax, G, D]
+ *   out          [B, H, D] fp64
+ */
+void oracle_decode_step(const void *q, const void *k_new, const void *v_new, void *k, void *v, int dtype,
+                        const int32_t *seqlens, int B, int H, int G, int D, int Tmax, double scale, int window,
+                        double *out)
+{
+    size_t es = elem_bytes(dtype);
+    int *len = (int *)malloc(sizeof(int) * (size_t)(B > 0 ? B : 1));
+    for (int b = 0; b < B; ++b) {
+        int L = clamp_len(seqlens[b], Tmax);
+        if (k_new && L < Tmax) {
+            size_t row = (size_t)G * D * es;                     /* one token, every group */
+            size_t dst = ((size_t)b * Tmax + L) * row;           /* k[b, L, 0, 0] */
+            memcpy((char *)k + dst, (const char *)k_new + (size_t)b * row, row);
+            memcpy((char *)v + dst, (const char *)v_new + (size_t)b * row, row);
+            L = L + 1;
+        }
+        len[b] = L;
+    }
+    int64_t rows = (int64_t)B * H;
+    int64_t row;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (row = 0; row < rows; ++row) {
+        int b = (int)(row / H), h = (int)(row % H);
+        int g = oracle_group_of_head(h, H, G);
+        int L = len[b];
+        int lo = (window > 0 && L > window) ? L - window : 0;    /* first admissible position */
+        int64_t key_stride = (int64_t)G * D;
+        int64_t key_base = ((int64_t)b * Tmax * G + g) * D + (int64_t)lo * key_stride;
+        attend_row(q, row * D, k, v, key_base, key_stride, L - lo, D, dtype, scale, out + row * D, NULL);
+    }
+    free(len);
+}
+
+/* Causal prefill with a sliding window: query position t attends to key
+ * positions [max(0, t + 1 - window), t], the `window` most recent ones with
+ * itself included (window = 0: every s <= t, the plain causal mask of [KB]
+ * section 3). Rows as in oracle_prefill. */
+void oracle_prefill_window(const void *q, const void *k, const void *v, int dtype, int B, int T, int H,
+                           int G, int D, int window, const int32_t *rows_b, const int32_t *rows_t,
+                           const int32_t *rows_h, int64_t n_rows, double *out)
+{
+    int64_t rows = rows_b ? n_rows : (int64_t)B * T * H;
+    double inv_sqrt_d = 1.0 / sqrt((double)D);
+    int64_t row;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (row = 0; row < rows; ++row) {
+        int b, t, h;
+        if (rows_b) {
+            b = rows_b[row];
+            t = rows_t[row];
+            h = rows_h[row];
+        } else {
+            b = (int)(row / ((int64_t)T * H));
+            t = (int)((row / H) % T);
+            h = (int)(row % H);
+        }
+        int g = oracle_group_of_head(h, H, G);
+        int lo = (window > 0 && t + 1 > window) ? t + 1 - window : 0;
+        int64_t q_off = (((int64_t)b * T + t) * H + h) * D;
+        int64_t key_base = (((int64_t)b * T + lo) * G + g) * D;
+        attend_row(q, q_off, k, v, key_base, (int64_t)G * D, t + 1 - lo, D, dtype, inv_sqrt_d, out + row * D,
+                   NULL);
+    }
+}
+
+/* Weighted conversion of key/value heads into G groups ([KB] section 4,
+ * Empirical evidence, the Chinchilla-scale reproduction, which proposes
+ * combining the heads of a group with per-head learned weights instead of the
+ * plain mean): group g is sum_i w[i] * in[n, i, :] over the heads i assigned
+ * to g by g(i). w = 1/r for every head is the mean-pool below.
+ *
+ *   in [N, H, D];  w [H] fp64;  out [N, G, D] fp64
+ */
+void oracle_weighted_pool(const void *in, int dtype, int64_t N, int H, int G, int D, const double *w,
+                          double *out)
+{
+    int64_t n;
+#pragma omp parallel for schedule(static)
+    for (n = 0; n < N; ++n) {
+        for (int g = 0; g < G; ++g) {
+            double *o = out + (n * G + g) * D;
+            for (int d = 0; d < D; ++d)
+                o[d] = 0.0;
+            for (int i = 0; i < H; ++i) {
+                if (oracle_group_of_head(i, H, G) != g)
+                    continue;
+                for (int d = 0; d < D; ++d)
+                    o[d] += w[i] * widen(in, (n * H + i) * D + d, dtype);
+            }
+        }
     }
 }
 

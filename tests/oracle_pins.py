@@ -19,7 +19,16 @@ What each pin compares against:
     row t equals decode over the first t+1 positions;
   * mean-pooling: a hand-worked example, identity at G = H, the all-head mean
     at G = 1, numpy's reshape-mean over contiguous groups, and linearity
-    (pooling weights then projecting equals projecting then pooling).
+    (pooling weights then projecting equals projecting then pooling);
+  * fp16 storage: all 65536 bit patterns against numpy's float16 widening;
+  * cache append: the caches after the call against numpy assignment, the
+    output against library attention over the appended cache, and the exact
+    new value for an empty sequence;
+  * sliding windows: library attention over the sliced cache (decode) or with
+    a band mask (prefill), the exact value for a one-position window, and no
+    change for a window covering the whole sequence;
+  * weighted pooling: numpy's einsum, one-hot weights (exact head copies) and
+    the mean at w = 1/r.
 """
 from __future__ import annotations
 
@@ -310,6 +319,105 @@ def pin_mean_pool(lib):
     np.testing.assert_allclose(h @ pooled_w, pooled_k, rtol=0, atol=1e-12)
 
 
+def pin_f16_widen(lib):
+    # every one of the 65536 fp16 bit patterns widens to numpy's own float16
+    # -> float64 conversion (G = H pooling copies each value through)
+    x = np.arange(65536, dtype=np.uint16).view(np.float16).reshape(64, 8, 128)
+    assert np.array_equal(O.mean_pool(x, 8, lib=lib), x.astype(np.float64), equal_nan=True)
+    # fp16 storage through decode equals library attention on the widened values
+    rng = np.random.default_rng(11)
+    B, H, G, D, Tmax = 2, 4, 2, 16, 9
+    q = rng.standard_normal((B, H, D)).astype(np.float16)
+    k = rng.standard_normal((B, Tmax, G, D)).astype(np.float16)
+    v = rng.standard_normal((B, Tmax, G, D)).astype(np.float16)
+    v.reshape(-1)[:6] = np.array([65504.0, -0.0, 6.1035156e-05, 5.9604645e-08, -2.0, 0.33325195], np.float16)
+    sl = np.array([9, 4], dtype=np.int32)
+    out = O.decode(q, k, v, sl, 0.25, lib=lib)
+    for b in range(B):
+        ref = _sdpa_decode(q[b].astype(np.float64), k[b].astype(np.float64), v[b].astype(np.float64),
+                           int(sl[b]), 0.25)
+        np.testing.assert_allclose(out[b], ref, rtol=1e-12, atol=1e-9)
+
+
+def pin_decode_append(lib):
+    rng = np.random.default_rng(12)
+    B, H, G, D, Tmax = 5, 8, 2, 16, 10
+    q, k, v = _rand(rng, B, H, D), _rand(rng, B, Tmax, G, D), _rand(rng, B, Tmax, G, D)
+    kn, vn = _rand(rng, B, G, D), _rand(rng, B, G, D)
+    sl = np.array([0, 3, 9, 10, -4], dtype=np.int32)  # empty, middle, last free slot, full, negative
+    for W in (0, 2):
+        out, ka, va = O.decode_step(q, k, v, sl, 0.3, k_new=kn, v_new=vn, window=W, lib=lib)
+        for b in range(B):
+            L = min(max(int(sl[b]), 0), Tmax)
+            ek, ev = k[b].copy(), v[b].copy()
+            if L < Tmax:
+                ek[L], ev[L] = kn[b], vn[b]
+                L += 1
+            assert np.array_equal(ka[b], ek) and np.array_equal(va[b], ev)  # only position L_b written
+            lo = max(0, L - W) if W else 0
+            np.testing.assert_allclose(out[b], _sdpa_decode(q[b], ek[lo:], ev[lo:], L - lo, 0.3),
+                                       rtol=1e-12, atol=1e-12)
+        # an empty sequence attends to the new token alone: its value, exactly
+        assert np.array_equal(out[0], np.repeat(vn[0], H // G, axis=0))
+        assert np.array_equal(out[4], np.repeat(vn[4], H // G, axis=0))
+
+
+def pin_decode_window(lib):
+    rng = np.random.default_rng(13)
+    B, H, G, D, Tmax = 3, 6, 3, 8, 12
+    q, k, v = _rand(rng, B, H, D), _rand(rng, B, Tmax, G, D), _rand(rng, B, Tmax, G, D)
+    sl = np.array([12, 5, 1], dtype=np.int32)
+    full = O.decode(q, k, v, sl, 0.4, lib=lib)
+    for W in (1, 3, 5, 12, 20):
+        out, ka, _ = O.decode_step(q, k, v, sl, 0.4, window=W, lib=lib)
+        assert np.array_equal(ka, k)  # no append: the cache is untouched
+        for b in range(B):
+            L = int(sl[b])
+            lo = max(0, L - W)
+            np.testing.assert_allclose(out[b], _sdpa_decode(q[b], k[b, lo:], v[b, lo:], L - lo, 0.4),
+                                       rtol=1e-12, atol=1e-12)
+            if W == 1:  # one key: its value, exactly
+                assert np.array_equal(out[b], np.repeat(v[b, L - 1], H // G, axis=0))
+            if W >= L:  # a window covering the sequence changes nothing
+                np.testing.assert_allclose(out[b], full[b], rtol=1e-13, atol=1e-13)
+
+
+def pin_prefill_window(lib):
+    rng = np.random.default_rng(14)
+    B, T, H, G, D = 2, 13, 4, 2, 8
+    q, k, v = _rand(rng, B, T, H, D), _rand(rng, B, T, G, D), _rand(rng, B, T, G, D)
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(H // G, dim=1)
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(H // G, dim=1)
+    i = torch.arange(T)
+    for W in (1, 4, 13, 30):
+        out = O.prefill_window(q, k, v, W, lib=lib)
+        band = (i[None, :] <= i[:, None]) & (i[None, :] > i[:, None] - W)  # key s in [t-W+1, t]
+        ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=band).permute(0, 2, 1, 3).numpy()
+        np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+        if W == 1:  # each query sees only itself
+            assert np.array_equal(out, np.repeat(v, H // G, axis=2))
+    rb, rt, rh = np.array([1, 0, 1]), np.array([12, 5, 0]), np.array([3, 0, 2])
+    np.testing.assert_array_equal(O.prefill_window(q, k, v, 4, rows=(rb, rt, rh), lib=lib),
+                                  O.prefill_window(q, k, v, 4, lib=lib)[rb, rt, rh])
+
+
+def pin_weighted_pool(lib):
+    rng = np.random.default_rng(15)
+    N, H, G, D = 5, 8, 2, 6
+    r = H // G
+    x = _rand(rng, N, H, D)
+    w = rng.standard_normal(H)
+    ref = np.einsum("ngjd,gj->ngd", x.reshape(N, G, r, D), w.reshape(G, r))
+    np.testing.assert_allclose(O.weighted_pool(x, G, w, lib=lib), ref, rtol=1e-13, atol=1e-13)
+    for j in range(r):  # one-hot weights pick head j of every group, exactly
+        oh = np.zeros(H)
+        oh[j::r] = 1.0
+        assert np.array_equal(O.weighted_pool(x, G, oh, lib=lib), x[:, j::r, :])
+    np.testing.assert_allclose(O.weighted_pool(x, G, np.full(H, 1.0 / r), lib=lib),
+                               x.reshape(N, G, r, D).mean(axis=2), rtol=0, atol=1e-14)
+
+
 PINS = [
     pin_group_map,
     pin_cache_golden,
@@ -323,4 +431,9 @@ PINS = [
     pin_permutation,
     pin_prefill,
     pin_mean_pool,
+    pin_f16_widen,
+    pin_decode_append,
+    pin_decode_window,
+    pin_prefill_window,
+    pin_weighted_pool,
 ]

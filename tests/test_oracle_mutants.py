@@ -28,6 +28,17 @@ MUTANTS = [
     ("bf16_low_half", "<< 16;\n        float f;", ";\n        float f;"),
     ("prefill_wrong_group", "int g = oracle_group_of_head(h, H, G);\n        int L = causal",
      "int g = h % G;\n        int L = causal"),
+    ("f16_exponent_bias", "mag = ldexp((double)(frac + 1024), ex - 25);", "mag = ldexp((double)(frac + 1024), ex - 24);"),
+    ("f16_subnormal_scale", "mag = ldexp((double)frac, -24);", "mag = ldexp((double)frac, -25);"),
+    ("append_overwrites_last", "size_t dst = ((size_t)b * Tmax + L) * row;",
+     "size_t dst = ((size_t)b * Tmax + (L > 0 ? L - 1 : 0)) * row;"),
+    ("append_not_attended", "            L = L + 1;\n", ""),
+    ("window_one_short", "int lo = (window > 0 && L > window) ? L - window : 0;",
+     "int lo = (window > 0 && L > window) ? L - window + 1 : 0;"),
+    ("prefill_window_one_long", "int lo = (window > 0 && t + 1 > window) ? t + 1 - window : 0;",
+     "int lo = (window > 0 && t + 1 > window) ? t - window : 0;"),
+    ("prefill_window_scale", "double inv_sqrt_d = 1.0 / sqrt((double)D);", "double inv_sqrt_d = 1.0 / (double)D;"),
+    ("weighted_pool_ignores_weights", "o[d] += w[i] * widen(in,", "o[d] += widen(in,"),
 ]
 
 
