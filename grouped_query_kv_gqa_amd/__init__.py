@@ -52,11 +52,13 @@ def load_library():
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
     lib.gqa_decode.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp]
     lib.gqa_decode_ex.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, i32]
+    lib.gqa_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, i32, vp, vp]
     lib.gqa_prefill.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.gqa_mean_pool_kv.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp]
     lib.gqa_decode_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32),
                                     ctypes.POINTER(i32), ctypes.POINTER(i64)]
-    for fn in ("gqa_decode", "gqa_decode_ex", "gqa_prefill", "gqa_mean_pool_kv", "gqa_decode_plan"):
+    for fn in ("gqa_decode", "gqa_decode_ex", "gqa_decode_step", "gqa_prefill", "gqa_mean_pool_kv",
+               "gqa_decode_plan"):
         getattr(lib, fn).restype = i32
     lib.gqa_status_string.argtypes = [i32]
     lib.gqa_status_string.restype = ctypes.c_char_p
@@ -123,6 +125,49 @@ def decode(q, k_cache, v_cache, seqlens, scale: float | None = None, out=None, s
         _check(lib.gqa_decode_ex(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr(),
                                  B, H, G, D, Tmax, float(scale), _dtype_code(q), out.data_ptr(),
                                  _stream_ptr(dev), int(split_tokens)))
+    return out
+
+
+def decode_step(q, k_cache, v_cache, seqlens, scale: float | None = None, k_new=None, v_new=None, window: int = 0,
+                out=None, split_tokens: int = 0):
+    """One decode step with an optional cache append and sliding window.
+    k_new, v_new [B,G,D] (or None): written into the caches at position
+    clamp(seqlens[b]) when that is below Tmax, and attended as the newest
+    position; seqlens is not advanced. window > 0: only the `window` newest
+    positions are read. Returns out [B,H,D]."""
+    lib = load_library()
+    B, H, D = q.shape
+    Bk, Tmax, G, Dk = k_cache.shape
+    if (Bk, Dk) != (B, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch between q, k_cache and v_cache")
+    if seqlens.dtype != torch.int32 or tuple(seqlens.shape) != (B,):
+        raise ValueError("seqlens must be int32 of shape [B]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share a dtype")
+    tensors = [q, k_cache, v_cache, seqlens]
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        if tuple(k_new.shape) != (B, G, D) or tuple(v_new.shape) != (B, G, D):
+            raise ValueError("k_new and v_new must be [B, G, d_h]")
+        if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+            raise TypeError("k_new and v_new must share q's dtype")
+        tensors += [k_new, v_new]
+    dev = _need_device(*tensors)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_device(out)
+        if out.shape != q.shape or out.dtype != q.dtype or out.device != dev:
+            raise ValueError("out must match q")
+    if scale is None:
+        scale = D ** -0.5
+    kn = k_new.data_ptr() if k_new is not None else None
+    vn = v_new.data_ptr() if v_new is not None else None
+    with torch.cuda.device(dev):
+        _check(lib.gqa_decode_step(q.data_ptr(), kn, vn, k_cache.data_ptr(), v_cache.data_ptr(),
+                                   seqlens.data_ptr(), B, H, G, D, Tmax, float(scale), int(window),
+                                   int(split_tokens), _dtype_code(q), out.data_ptr(), _stream_ptr(dev)))
     return out
 
 

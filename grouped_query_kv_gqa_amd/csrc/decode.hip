@@ -83,6 +83,26 @@ __device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t x, int lane)
     return x;
 }
 
+// The cache positions one decode step reads for a sequence: [lo, lo + n).
+// L0 = clamp(seqlens[b], 0, Tmax). With append, a sequence whose cache is not
+// full gains the new token at position L0 (read from k_new/v_new, written to
+// the cache), so it holds L = L0 + 1 positions; a full one keeps Tmax. A
+// sliding window keeps the `window` newest positions: lo = max(0, L - window).
+// The appended token, when there is one, is the last of the n positions.
+struct Span {
+    int lo, n;
+    bool appended;
+};
+
+__device__ __forceinline__ Span seq_span(int32_t s, int Tmax, int append, int window)
+{
+    const int L0 = clamp_len(s, Tmax);
+    const bool app = append && L0 < Tmax;
+    const int L = L0 + (app ? 1 : 0);
+    const int lo = (window > 0 && L > window) ? L - window : 0;
+    return {lo, L - lo, app};
+}
+
 // Flat-position partition shared by the decode and merge kernels (both must
 // compute identical values): total positions and the piece length P.
 struct Partition {
@@ -90,12 +110,12 @@ struct Partition {
     int64_t P;
 };
 
-__device__ __forceinline__ Partition make_partition(const int32_t *seqlens, int B, int Tmax, int nwg, int fixed_P,
-                                                    int lane)
+__device__ __forceinline__ Partition make_partition(const int32_t *seqlens, int B, int Tmax, int append, int window,
+                                                    int nwg, int fixed_P, int lane)
 {
     int64_t tot = 0;
     for (int i = lane; i < B; i += 64)
-        tot += clamp_len(seqlens[i], Tmax);
+        tot += seq_span(seqlens[i], Tmax, append, window).n;
     tot = wave_sum_i64(tot);
     int64_t P;
     if (fixed_P > 0) {
@@ -113,11 +133,16 @@ __device__ __forceinline__ Partition make_partition(const int32_t *seqlens, int 
 // heads [h0, h0 + nheads) of group g. The wave takes tiles ta + sub*32,
 // ta + (sub + WPG)*32, ... Writes the finished rows to `out` when `whole`,
 // else a normalised partial row per head and its base-2 log-sum-exp.
-template <int D, int NT, int WPG>
-__device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, const __bf16 *kc, const __bf16 *vc,
-                                             int b, int g, int h0, int nheads, int ta, int tb, bool whole, int H,
-                                             int G, int Tmax, int sub, float scale_log2, __bf16 *vl,
-                                             __bf16 *__restrict__ out, float *__restrict__ part_row,
+//
+// APPEND: position t_new (relative to the span, or -1) is the appended token:
+// its rows come from knew_row/vnew_row (this group's slice of k_new, v_new)
+// and, when store_new, are written to the cache at that position.
+template <int D, int NT, int WPG, bool APPEND>
+__device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, int b, int g,
+                                             int h0, int nheads, int t_off, int ta, int tb, int t_new,
+                                             const __bf16 *knew_row, const __bf16 *vnew_row, bool store_new,
+                                             bool whole, int H, int G, int Tmax, int sub, float scale_log2,
+                                             __bf16 *vl, __bf16 *__restrict__ out, float *__restrict__ part_row,
                                              float *__restrict__ lse_row, int64_t part_stride, int lane)
 {
     using C = TileCfg<D, NT>;
@@ -139,8 +164,8 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, const
     }
 
     const int64_t tok_stride = (int64_t)G * D;
-    const __bf16 *kbase = kc + ((int64_t)b * Tmax * G + g) * D;
-    const __bf16 *vbase = vc + ((int64_t)b * Tmax * G + g) * D;
+    __bf16 *kbase = kc + (((int64_t)b * Tmax + t_off) * G + g) * D;  // span position 0
+    __bf16 *vbase = vc + (((int64_t)b * Tmax + t_off) * G + g) * D;
 
     float m_run[NT], l_run[NT];
     f32x4_t acc[NT][C::DT];
@@ -162,16 +187,22 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, const
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             const int t = min(t0 + mt * 16 + col, t_last);
+            const __bf16 *src = kbase + t * tok_stride;
+            if constexpr (APPEND)
+                src = (t == t_new) ? knew_row : src;
 #pragma unroll
             for (int s = 0; s < C::KS; ++s)
-                kr[mt][s] = load16(kbase + t * tok_stride + (s * 4 + kb) * 8);
+                kr[mt][s] = load16(src + (s * 4 + kb) * 8);
         }
     };
     auto load_v = [&](int t0, u32x4_t (&vr)[C::VLOADS]) {
 #pragma unroll
         for (int i = 0; i < C::VLOADS; ++i) {
             const int t = min(t0 + i * C::VROWS + lane / C::CH, t_last);
-            vr[i] = load16(vbase + t * tok_stride + (lane % C::CH) * 8);
+            const __bf16 *src = vbase + t * tok_stride;
+            if constexpr (APPEND)
+                src = (t == t_new) ? vnew_row : src;
+            vr[i] = load16(src + (lane % C::CH) * 8);
         }
     };
 
@@ -203,6 +234,18 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, const
                     c = mfma16x16x32(__builtin_bit_cast(bf16x8_t, kbuf[mt][s]), qf[nt][s], c);
                 st[mt][nt] = c;
             }
+        if constexpr (APPEND) {
+            // the lanes holding the appended token's key row store it
+            if (store_new && t_new >= t0 && t_new < t0 + kTile) {
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+                    if (t0 + mt * 16 + col == t_new) {
+#pragma unroll
+                        for (int s = 0; s < C::KS; ++s)
+                            *reinterpret_cast<u32x4_t *>(kbase + t_new * tok_stride + (s * 4 + kb) * 8) = kbuf[mt][s];
+                    }
+            }
+        }
         compiler_fence();
         __builtin_amdgcn_sched_barrier(0);
         load_k(tn, kbuf);  // clamped prefetch, also past the end
@@ -217,6 +260,10 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, const
             const u32x4_t zero = {0, 0, 0, 0};
             *reinterpret_cast<u32x4_t *>(vl + tl * C::LDS_STRIDE + (lane % C::CH) * 8) =
                 (t0 + tl < tb) ? vbuf[i] : zero;
+            if constexpr (APPEND) {
+                if (store_new && t0 + tl == t_new)
+                    *reinterpret_cast<u32x4_t *>(vbase + t_new * tok_stride + (lane % C::CH) * 8) = vbuf[i];
+            }
         }
         compiler_fence();
         __builtin_amdgcn_sched_barrier(0);
@@ -311,12 +358,12 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, const
     }
 }
 
-template <int D, int NT, int WAVES, int GB>
+template <int D, int NT, int WAVES, int GB, bool APPEND>
 __global__ void __launch_bounds__(WAVES * 64)
-decode_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kc, const __bf16 *vc,
-                   const int32_t *__restrict__ seqlens, int B, int H, int G, int Tmax, int r, int head_tiles,
-                   float scale_log2, int nwg, int fixed_P, __bf16 *__restrict__ out, float *__restrict__ part,
-                   float *__restrict__ lse)
+decode_bf16_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const __bf16 *__restrict__ knew,
+                   const __bf16 *__restrict__ vnew, const int32_t *__restrict__ seqlens, int B, int H, int G,
+                   int Tmax, int window, int r, int head_tiles, float scale_log2, int nwg, int fixed_P,
+                   __bf16 *__restrict__ out, float *__restrict__ part, float *__restrict__ lse)
 {
     constexpr int WPG = WAVES / GB;
     using C = TileCfg<D, NT>;
@@ -331,7 +378,7 @@ decode_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kc, const __bf16 
     const int h0 = g * r + ht * C::HEADS;
     const int nheads = min(C::HEADS, r - ht * C::HEADS);
 
-    const Partition pt = make_partition(seqlens, B, Tmax, nwg, fixed_P, lane);
+    const Partition pt = make_partition(seqlens, B, Tmax, APPEND, window, nwg, fixed_P, lane);
     const int64_t lo = (int64_t)k * pt.P;
     if (lo >= pt.total)
         return;
@@ -340,7 +387,10 @@ decode_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kc, const __bf16 
     // Walk the sequences overlapping [lo, hi), 64 lengths at a time.
     int64_t pre = 0;
     for (int b0 = 0; b0 < B; b0 += 64) {
-        const int Lc = (b0 + lane < B) ? clamp_len(seqlens[b0 + lane], Tmax) : 0;
+        Span sp = {0, 0, false};
+        if (b0 + lane < B)
+            sp = seq_span(seqlens[b0 + lane], Tmax, APPEND, window);
+        const int Lc = sp.n;
         const int64_t incl = wave_incl_scan_i64(Lc, lane);
         const int64_t chunk_total = __shfl(incl, 63, 64);
         if (pre + chunk_total <= lo) {
@@ -362,8 +412,12 @@ decode_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kc, const __bf16 
             const int64_t piece = (int64_t)k + b;
             // partial layout [piece][head][sub][d], log-sum-exp [piece][head][sub]
             const int64_t slot = (piece * H + h0) * WPG + sub;
-            decode_piece<D, NT, WPG>(q, kc, vc, b, g, h0, nheads, ta, tb, whole, H, G, Tmax, sub, scale_log2,
-                                     &vlds[wave][0], out, part + slot * D, lse + slot, WPG, lane);
+            const int lo_b = __shfl(sp.lo, i, 64);
+            const int t_new = (APPEND && __shfl((int)sp.appended, i, 64)) ? L - 1 : -1;
+            const int64_t new_off = ((int64_t)b * G + g) * D;
+            decode_piece<D, NT, WPG, APPEND>(q, kc, vc, b, g, h0, nheads, lo_b, ta, tb, t_new, knew + new_off,
+                                             vnew + new_off, ht == 0, whole, H, G, Tmax, sub, scale_log2,
+                                             &vlds[wave][0], out, part + slot * D, lse + slot, WPG, lane);
         }
         pre += chunk_total;
     }
@@ -378,8 +432,9 @@ decode_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kc, const __bf16 
 // empty sequences; rows that the decode kernel wrote whole are skipped.
 template <int D, int NQ>
 __global__ void __launch_bounds__(256)
-decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax, int nwg, int fixed_P, int wpg,
-                    const float *__restrict__ part, const float *__restrict__ lse, __bf16 *__restrict__ out)
+decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax, int append, int window, int nwg,
+                    int fixed_P, int wpg, const float *__restrict__ part, const float *__restrict__ lse,
+                    __bf16 *__restrict__ out)
 {
     constexpr int DCH = 4 * NQ;      // d values per item
     constexpr int NDC = D / DCH;     // items per row
@@ -393,7 +448,7 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
     // partition and this sequence's first flat position (each wave on its own)
     int64_t tot = 0, pre = 0;
     for (int i = lane; i < B; i += 64) {
-        const int Li = clamp_len(seqlens[i], Tmax);
+        const int Li = seq_span(seqlens[i], Tmax, append, window).n;
         tot += Li;
         if (i < b)
             pre += Li;
@@ -414,7 +469,7 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
     const int sl = lane / NQ, qd = lane % NQ;
     const int d0 = dc * DCH + qd * 4;
     __bf16 *dst = out + ((int64_t)b * H + h) * D + d0;
-    const int L = clamp_len(seqlens[b], Tmax);
+    const int L = seq_span(seqlens[b], Tmax, append, window).n;
     if (L == 0) {
         if (sl == 0)
             *reinterpret_cast<u32x2_t *>(dst) = (u32x2_t){0, 0};
@@ -482,8 +537,9 @@ hipError_t launch_merge(const DecodePlan &p, const DecodeArgs &a, int wpg)
 {
     constexpr int NDC = D / (4 * NQ);
     dim3 grid((unsigned)((a.H * NDC + 3) / 4), (unsigned)a.B);
-    decode_merge_kernel<D, NQ><<<grid, 256, 0, a.stream>>>(a.seqlens, a.B, a.H, a.Tmax, p.nwg, p.fixed_P, wpg,
-                                                          a.part, a.lse, static_cast<__bf16 *>(a.out));
+    decode_merge_kernel<D, NQ><<<grid, 256, 0, a.stream>>>(a.seqlens, a.B, a.H, a.Tmax, a.knew != nullptr,
+                                                          a.window, p.nwg, p.fixed_P, wpg, a.part, a.lse,
+                                                          static_cast<__bf16 *>(a.out));
     return hipGetLastError();
 }
 
@@ -504,16 +560,19 @@ hipError_t launch_merge_d(const DecodePlan &p, const DecodeArgs &a, int wpg)
 // wave walks the cache one position at a time with an online softmax.
 template <int D>
 __global__ void __launch_bounds__(64)
-decode_f32_kernel(const float *__restrict__ q, const float *__restrict__ kc, const float *__restrict__ vc,
-                  const int32_t *__restrict__ seqlens, int H, int G, int Tmax, int r, float scale,
-                  float *__restrict__ out)
+decode_f32_kernel(const float *__restrict__ q, float *kc, float *vc, const float *__restrict__ knew,
+                  const float *__restrict__ vnew, const int32_t *__restrict__ seqlens, int H, int G, int Tmax,
+                  int append, int window, int r, float scale, float *__restrict__ out)
 {
     constexpr int J = D / 64;
     const int64_t row = blockIdx.x;
     const int b = (int)(row / H), h = (int)(row % H);
     const int g = h / r;
     const int lane = threadIdx.x;
-    const int L = clamp_len(seqlens[b], Tmax);
+    const Span sp = seq_span(seqlens[b], Tmax, append, window);
+    const int L = sp.n;
+    const int t_new = sp.appended ? L - 1 : -1;  // span position of the appended token
+    const int64_t new_off = ((int64_t)b * G + g) * D;
     float qv[J], acc[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -522,8 +581,9 @@ decode_f32_kernel(const float *__restrict__ q, const float *__restrict__ kc, con
     }
     float m = -INFINITY, l = 0.f;
     for (int t = 0; t < L; ++t) {
-        const float *kp = kc + (((int64_t)b * Tmax + t) * G + g) * D;
-        const float *vp = vc + (((int64_t)b * Tmax + t) * G + g) * D;
+        const int64_t off = (((int64_t)b * Tmax + sp.lo + t) * G + g) * D;
+        const float *kp = (t == t_new) ? knew + new_off : kc + off;
+        const float *vp = (t == t_new) ? vnew + new_off : vc + off;
         float dot = 0.f;
 #pragma unroll
         for (int j = 0; j < J; ++j)
@@ -541,22 +601,39 @@ decode_f32_kernel(const float *__restrict__ q, const float *__restrict__ kc, con
 #pragma unroll
     for (int j = 0; j < J; ++j)
         out[row * D + lane + 64 * j] = L > 0 ? acc[j] / l : 0.f;
+    if (t_new >= 0 && h % r == 0) {  // the group's first head stores the appended token
+        const int64_t off = (((int64_t)b * Tmax + sp.lo + t_new) * G + g) * D;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            kc[off + lane + 64 * j] = knew[new_off + lane + 64 * j];
+            vc[off + lane + 64 * j] = vnew[new_off + lane + 64 * j];
+        }
+    }
 }
 
 template <int D, int NT, int WAVES, int GB>
 const void *bf16_symbol()
 {
-    return reinterpret_cast<const void *>(&decode_bf16_kernel<D, NT, WAVES, GB>);
+    return reinterpret_cast<const void *>(&decode_bf16_kernel<D, NT, WAVES, GB, false>);
 }
 
 template <int D, int NT, int WAVES, int GB>
 hipError_t launch_bf16(const DecodePlan &p, const DecodeArgs &a)
 {
     dim3 grid(p.nwg, (a.G / GB) * p.head_tiles);
-    decode_bf16_kernel<D, NT, WAVES, GB><<<grid, WAVES * 64, 0, a.stream>>>(
-        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), static_cast<const __bf16 *>(a.v),
-        a.seqlens, a.B, a.H, a.G, a.Tmax, p.r, p.head_tiles, a.scale * kLog2e, p.nwg, p.fixed_P,
-        static_cast<__bf16 *>(a.out), a.part, a.lse);
+    // The caches are written only when appending (a.knew set).
+    __bf16 *kc = const_cast<__bf16 *>(static_cast<const __bf16 *>(a.k));
+    __bf16 *vc = const_cast<__bf16 *>(static_cast<const __bf16 *>(a.v));
+    const __bf16 *q = static_cast<const __bf16 *>(a.q);
+    const __bf16 *kn = static_cast<const __bf16 *>(a.knew), *vn = static_cast<const __bf16 *>(a.vnew);
+    if (a.knew)
+        decode_bf16_kernel<D, NT, WAVES, GB, true><<<grid, WAVES * 64, 0, a.stream>>>(
+            q, kc, vc, kn, vn, a.seqlens, a.B, a.H, a.G, a.Tmax, a.window, p.r, p.head_tiles, a.scale * kLog2e,
+            p.nwg, p.fixed_P, static_cast<__bf16 *>(a.out), a.part, a.lse);
+    else
+        decode_bf16_kernel<D, NT, WAVES, GB, false><<<grid, WAVES * 64, 0, a.stream>>>(
+            q, kc, vc, kn, vn, a.seqlens, a.B, a.H, a.G, a.Tmax, a.window, p.r, p.head_tiles, a.scale * kLog2e,
+            p.nwg, p.fixed_P, static_cast<__bf16 *>(a.out), a.part, a.lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -594,14 +671,17 @@ hipError_t launch_decode(const DecodePlan &p, const DecodeArgs &a, gqa_dtype dty
 {
     if (dtype == GQA_FP32) {
         dim3 grid((unsigned)((int64_t)a.B * a.H));
+        const float *q = static_cast<const float *>(a.q);
+        float *kc = const_cast<float *>(static_cast<const float *>(a.k));
+        float *vc = const_cast<float *>(static_cast<const float *>(a.v));
+        const float *kn = static_cast<const float *>(a.knew), *vn = static_cast<const float *>(a.vnew);
+        const int app = a.knew != nullptr;
         if (a.D == 64)
-            decode_f32_kernel<64><<<grid, 64, 0, a.stream>>>(
-                static_cast<const float *>(a.q), static_cast<const float *>(a.k), static_cast<const float *>(a.v),
-                a.seqlens, a.H, a.G, a.Tmax, p.r, a.scale, static_cast<float *>(a.out));
+            decode_f32_kernel<64><<<grid, 64, 0, a.stream>>>(q, kc, vc, kn, vn, a.seqlens, a.H, a.G, a.Tmax, app,
+                                                             a.window, p.r, a.scale, static_cast<float *>(a.out));
         else
-            decode_f32_kernel<128><<<grid, 64, 0, a.stream>>>(
-                static_cast<const float *>(a.q), static_cast<const float *>(a.k), static_cast<const float *>(a.v),
-                a.seqlens, a.H, a.G, a.Tmax, p.r, a.scale, static_cast<float *>(a.out));
+            decode_f32_kernel<128><<<grid, 64, 0, a.stream>>>(q, kc, vc, kn, vn, a.seqlens, a.H, a.G, a.Tmax, app,
+                                                              a.window, p.r, a.scale, static_cast<float *>(a.out));
         return hipGetLastError();
     }
     return with_variant(p, a.D, [&]<int DD, int NTT, int WW, int GG>() { return launch_bf16<DD, NTT, WW, GG>(p, a); });

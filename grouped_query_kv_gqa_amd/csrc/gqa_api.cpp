@@ -115,14 +115,15 @@ gqa_status workspace_for(int device, hipStream_t stream, int64_t bytes, char **o
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-gqa_status gqa_decode_ex(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens, int B,
-                         int H, int G, int d_h, int Tmax, float scale, gqa_dtype dtype, void *out,
-                         hipStream_t stream, int split_tokens)
+gqa_status decode_impl(const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                       const void *v_cache, const int32_t *seqlens, int B, int H, int G, int d_h, int Tmax,
+                       float scale, int window, int split_tokens, gqa_dtype dtype, void *out, hipStream_t stream)
 {
     std::string err;
-    gqa_status s = gqa::check_decode(q, k_cache, v_cache, seqlens, B, H, G, d_h, Tmax, scale, dtype, out, &err);
+    gqa_status s = gqa::check_decode_step(q, k_new, v_new, k_cache, v_cache, seqlens, B, H, G, d_h, Tmax, scale,
+                                          window, dtype, out, &err);
     if (s != GQA_OK)
         return record(s, err);
     if (split_tokens < 0)
@@ -146,7 +147,8 @@ gqa_status gqa_decode_ex(const void *q, const void *k_cache, const void *v_cache
     if ((int64_t)(G / plan.gb) * plan.head_tiles > 65535)
         return record(GQA_ERR_UNSUPPORTED, "too many key/value heads");
 
-    gqa::DecodeArgs a{q, k_cache, v_cache, seqlens, B, H, G, d_h, Tmax, scale, out, nullptr, nullptr, stream};
+    gqa::DecodeArgs a{q, k_cache, v_cache, k_new, v_new, seqlens, B, H, G, d_h, Tmax, window, scale,
+                      out, nullptr, nullptr, stream};
     if (dtype == GQA_BF16) {
         int bpc = 0;
         if ((s = blocks_per_cu(device, plan, d_h, &bpc)) != GQA_OK)
@@ -163,6 +165,27 @@ gqa_status gqa_decode_ex(const void *q, const void *k_cache, const void *v_cache
     if (e != hipSuccess)
         return hip_failure(e, "decode launch");
     return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+
+gqa_status gqa_decode_ex(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens, int B,
+                         int H, int G, int d_h, int Tmax, float scale, gqa_dtype dtype, void *out,
+                         hipStream_t stream, int split_tokens)
+{
+    return decode_impl(q, nullptr, nullptr, k_cache, v_cache, seqlens, B, H, G, d_h, Tmax, scale, 0, split_tokens,
+                       dtype, out, stream);
+}
+
+gqa_status gqa_decode_step(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                           const int32_t *seqlens, int B, int H, int G, int d_h, int Tmax, float scale, int window,
+                           int split_tokens, gqa_dtype dtype, void *out, hipStream_t stream)
+{
+    return decode_impl(q, k_new, v_new, k_cache, v_cache, seqlens, B, H, G, d_h, Tmax, scale, window, split_tokens,
+                       dtype, out, stream);
 }
 
 gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens, int B,

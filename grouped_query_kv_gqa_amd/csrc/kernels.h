@@ -8,9 +8,11 @@
 namespace gqa {
 
 struct DecodeArgs {
-    const void *q, *k, *v;
+    const void *q, *k, *v;          // k, v are written (position L_b) only when knew is set
+    const void *knew, *vnew;        // appended token [B, G, D], or null
     const int32_t *seqlens;
     int B, H, G, D, Tmax;
+    int window;                     // 0: every position
     float scale;
     void *out;
     float *part;  // partial rows (bf16 path)

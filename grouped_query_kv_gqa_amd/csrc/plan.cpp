@@ -82,6 +82,40 @@ gqa_status check_decode(const void *q, const void *k, const void *v, const int32
     return GQA_OK;
 }
 
+gqa_status check_decode_step(const void *q, const void *k_new, const void *v_new, const void *k, const void *v,
+                             const int32_t *seqlens, int B, int H, int G, int d_h, int Tmax, float scale, int window,
+                             gqa_dtype dtype, const void *out, std::string *err)
+{
+    gqa_status s = check_decode(q, k, v, seqlens, B, H, G, d_h, Tmax, scale, dtype, out, err);
+    if (s != GQA_OK)
+        return s;
+    if (window < 0)
+        return fail(err, GQA_ERR_INVALID_ARG, "window must be >= 0");
+    if ((k_new == nullptr) != (v_new == nullptr))
+        return fail(err, GQA_ERR_INVALID_ARG, "k_new and v_new must both be given or both be null");
+    if (B == 0 || !k_new)
+        return GQA_OK;
+    if (Tmax < 1)
+        return fail(err, GQA_ERR_INVALID_ARG, "appending needs Tmax >= 1");
+    if (!aligned16(k_new) || !aligned16(v_new))
+        return fail(err, GQA_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+    const int64_t e = elem_size(dtype);
+    const int64_t q_bytes = (int64_t)B * H * d_h * e;
+    const int64_t n_bytes = (int64_t)B * G * d_h * e;
+    const int64_t kv_bytes = (int64_t)B * Tmax * G * d_h * e;
+    if (ranges_overlap(out, q_bytes, k_new, n_bytes) || ranges_overlap(out, q_bytes, v_new, n_bytes))
+        return fail(err, GQA_ERR_INVALID_ARG, "out overlaps an input");
+    // the caches are written: they must not overlap each other or any input
+    const void *ins[] = {q, k_new, v_new, seqlens};
+    const int64_t in_bytes[] = {q_bytes, n_bytes, n_bytes, 4 * (int64_t)B};
+    if (ranges_overlap(k, kv_bytes, v, kv_bytes))
+        return fail(err, GQA_ERR_INVALID_ARG, "k_cache and v_cache overlap");
+    for (int i = 0; i < 4; ++i)
+        if (ranges_overlap(k, kv_bytes, ins[i], in_bytes[i]) || ranges_overlap(v, kv_bytes, ins[i], in_bytes[i]))
+            return fail(err, GQA_ERR_INVALID_ARG, "a cache overlaps q, k_new, v_new or seqlens");
+    return GQA_OK;
+}
+
 int default_blocks_per_cu(int d_h, int nt)
 {
     // gfx950 build: d_h = 64 with 32-head tiles runs two 4-wave workgroups per

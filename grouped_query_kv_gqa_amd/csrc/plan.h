@@ -42,6 +42,11 @@ gqa_status check_decode(const void *q, const void *k, const void *v, const int32
                         std::string *err);
 gqa_status plan_decode(int B, int H, int G, int d_h, int Tmax, gqa_dtype dtype, int split_tokens,
                        int cu_count, int blocks_per_cu, DecodePlan *plan, std::string *err);
+// check_decode plus the cache-append and window arguments of gqa_decode_step.
+gqa_status check_decode_step(const void *q, const void *k_new, const void *v_new, const void *k, const void *v,
+                             const int32_t *seqlens, int B, int H, int G, int d_h, int Tmax, float scale, int window,
+                             gqa_dtype dtype, const void *out, std::string *err);
+
 gqa_status check_prefill(const void *q, const void *k, const void *v, int B, int T, int H, int G, int d_h,
                          int causal, gqa_dtype dtype, const void *out, std::string *err);
 gqa_status check_mean_pool(const void *in, int64_t N, int H, int G, int d_h, gqa_dtype dtype,

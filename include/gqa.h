@@ -98,6 +98,37 @@ gqa_status gqa_decode_ex(const void *q, const void *k_cache, const void *v_cache
                          hipStream_t stream, int split_tokens);
 
 /*
+ * gqa_decode_step -- one decode step of a serving loop, with two optional
+ * variants: the new token's key and value are appended to the cache before
+ * it is read, and each query may see only a sliding window of the newest
+ * positions.
+ * Defines: "Grouped-Query Attention" (llm-arch-kb), section 1 Premise (a
+ * decode step reads every cached entry, the new token's included) and section
+ * 2 Derivation, Setup (head i attends over the keys and values cached so
+ * far); section 4 Empirical evidence, Mistral 7B ablation (GQA combined with
+ * sliding-window attention; the page gives no formula, the window below is
+ * this library's reading).
+ *
+ *   k_new, v_new  [B, G, d_h] the new token's key and value, or both NULL
+ *                 (no append). With them, for each b with L0 = clamp(seqlens[b],
+ *                 0, Tmax) < Tmax, k_new[b] and v_new[b] are written to cache
+ *                 position L0 and the sequence is attended over L0 + 1
+ *                 positions; a full cache (L0 = Tmax) is neither written nor
+ *                 extended. seqlens itself is not modified (the caller
+ *                 advances it).
+ *   k_cache, v_cache  as for gqa_decode, written at position L0 when
+ *                 appending; they must not overlap each other or any input.
+ *   window        0: every position; W > 0: only the W newest positions
+ *                 [max(0, L - W), L) of the (appended) sequence are read.
+ *   split_tokens  as for gqa_decode_ex.
+ * Other arguments, layouts and errors as for gqa_decode; window < 0 and one
+ * of k_new, v_new NULL without the other are GQA_ERR_INVALID_ARG.
+ */
+gqa_status gqa_decode_step(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                           const int32_t *seqlens, int B, int H, int G, int d_h, int Tmax, float scale, int window,
+                           int split_tokens, gqa_dtype dtype, void *out, hipStream_t stream);
+
+/*
  * gqa_prefill -- attention for every position of B sequences of length T.
  * Defines: "Grouped-Query Attention" (llm-arch-kb), section 3 Reference
  * implementation (sketch: q [B,T,H,d_h], k and v [B,T,G,d_h] broadcast to the

@@ -1,0 +1,121 @@
+"""GPU parity of gqa_decode_step (cache append and sliding window) against
+the fp64 oracle's decode_step, which writes the new token into host copies
+of the caches and then attends.
+
+Checked per case: the output to the bf16/fp32 tolerance, and the caches
+after the call bit for bit (only position clamp(seqlens[b]) of a sequence
+whose cache is not full may change). Inputs come from the seeded generators
+of grouped_query_kv_gqa_amd.inputs; the oracle reads host copies of the same
+bits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import grouped_query_kv_gqa_amd as gq
+import oracle as O
+from grouped_query_kv_gqa_amd import inputs as I
+from gpu_util import assert_parity, say, to_host
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _bits(t):
+    t = to_host(t)
+    return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+
+def _case(B, H, G, D, Tmax, seqlens, dtype, seed):
+    w = I.DecodeWorkload("step", B, H, G, D, Tmax, dtype)
+    x = I.decode_inputs(w, seed=seed, device=DEV, seqlens=seqlens)
+    kn = I.random_tensor((B, G, D), seed=seed + 1, dtype=dtype, device=DEV)
+    vn = I.random_tensor((B, G, D), seed=seed + 2, dtype=dtype, device=DEV)
+    return w, x, kn, vn
+
+
+def _check(w, x, kn, vn, window, split, append=True):
+    k0, v0 = x["k_cache"].clone(), x["v_cache"].clone()
+    ref, k_ref, v_ref = O.decode_step(to_host(x["q"]), to_host(k0), to_host(v0), to_host(x["seqlens"]), w.scale,
+                                      k_new=to_host(kn) if append else None, v_new=to_host(vn) if append else None,
+                                      window=window)
+    k, v = k0.clone(), v0.clone()
+    torch.cuda.synchronize()
+    out = gq.decode_step(x["q"], k, v, x["seqlens"], scale=w.scale, k_new=kn if append else None,
+                         v_new=vn if append else None, window=window, split_tokens=split)
+    torch.cuda.synchronize()
+    assert_parity(out, ref, w.dtype, f"window={window} split={split} append={append}")
+    assert np.array_equal(_bits(k), k_ref) and np.array_equal(_bits(v), v_ref), "cache contents after the call"
+
+
+STEP = [
+    # B, H, G, D, Tmax, seqlens, dtype
+    (5, 8, 2, 128, 300, [300, 0, 299, 37, -3], torch.bfloat16),   # full, empty, last free slot, middle, negative
+    (3, 32, 8, 128, 257, [100, 256, 1], torch.bfloat16),
+    (2, 8, 8, 64, 100, [64, 99], torch.bfloat16),                 # MHA
+    (2, 16, 1, 128, 130, [130, 32], torch.bfloat16),              # MQA
+    (2, 64, 1, 128, 96, [95, 31], torch.bfloat16),                # 64 heads in one group
+    (2, 24, 4, 64, 45, [44, 0], torch.bfloat16),
+    (3, 12, 3, 64, 50, [50, 17, 0], torch.float32),
+    (2, 4, 2, 128, 33, [32, 5], torch.float32),
+]
+
+
+@pytest.mark.parametrize("B,H,G,D,Tmax,seqlens,dtype", STEP)
+def test_decode_append_parity(B, H, G, D, Tmax, seqlens, dtype):
+    say(f"decode_step append B={B} H={H} G={G} D={D} Tmax={Tmax} {dtype}")
+    w, x, kn, vn = _case(B, H, G, D, Tmax, seqlens, dtype, seed=B * 100 + H + G)
+    for split in (0, 32, 64):
+        _check(w, x, kn, vn, 0, split)
+
+
+@pytest.mark.parametrize("B,H,G,D,Tmax,seqlens,dtype", STEP)
+@pytest.mark.parametrize("window", [1, 7, 64, 100000])
+def test_decode_window_parity(B, H, G, D, Tmax, seqlens, dtype, window):
+    say(f"decode_step window={window} B={B} H={H} G={G} D={D} Tmax={Tmax} {dtype}")
+    w, x, kn, vn = _case(B, H, G, D, Tmax, seqlens, dtype, seed=B * 100 + H + G + window)
+    _check(w, x, kn, vn, window, 32, append=False)
+    _check(w, x, kn, vn, window, 0, append=True)
+
+
+def test_decode_step_plain_matches_decode():
+    w = I.DecodeWorkload("plain", 3, 32, 8, 128, 700, torch.bfloat16)
+    say("decode_step without append or window equals gqa_decode")
+    x = I.decode_inputs(w, seed=5, device=DEV, seqlens=[700, 350, 1])
+    a = gq.decode(x["q"], x["k_cache"], x["v_cache"], x["seqlens"], scale=w.scale)
+    b = gq.decode_step(x["q"], x["k_cache"], x["v_cache"], x["seqlens"], scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_decode_append_llama3_8b_sampled():
+    """Full-size Llama-3-8B decode layer with every cache one short of full:
+    append + attend, checked on sampled sequences and on the written rows."""
+    base = I.WORKLOADS["decode_llama3_8b"]
+    say("decode_step append at full Llama-3-8B size")
+    x = I.decode_inputs(base, seed=0, device=DEV, seqlens=[base.Tmax - 1] * base.B)
+    kn = I.random_tensor((base.B, base.G, base.D), seed=11, dtype=base.dtype, device=DEV)
+    vn = I.random_tensor((base.B, base.G, base.D), seed=12, dtype=base.dtype, device=DEV)
+    out = gq.decode_step(x["q"], x["k_cache"], x["v_cache"], x["seqlens"], scale=base.scale, k_new=kn, v_new=vn)
+    torch.cuda.synchronize()
+    L = base.Tmax - 1
+    assert torch.equal(x["k_cache"][:, L], kn) and torch.equal(x["v_cache"][:, L], vn)
+    for b in (0, 9, 15):
+        ref = O.decode(to_host(x["q"][b:b + 1]), to_host(x["k_cache"][b:b + 1]), to_host(x["v_cache"][b:b + 1]),
+                       np.array([L + 1], np.int32), base.scale)
+        assert_parity(out[b:b + 1], ref, base.dtype, f"sequence {b}")
+
+
+def test_decode_step_errors():
+    say("decode_step argument errors")
+    w, x, kn, vn = _case(2, 8, 2, 64, 20, [3, 4], torch.bfloat16, seed=1)
+    with pytest.raises(gq.GqaError):
+        gq.decode_step(x["q"], x["k_cache"], x["v_cache"], x["seqlens"], window=-1)
+    with pytest.raises(ValueError):
+        gq.decode_step(x["q"], x["k_cache"], x["v_cache"], x["seqlens"], k_new=kn)
+    alias = x["k_cache"].view(-1)[: kn.numel()].view(kn.shape)  # contiguous view into the key cache
+    with pytest.raises(gq.GqaError):  # a written cache aliasing the new token
+        gq.decode_step(x["q"], x["k_cache"], x["v_cache"], x["seqlens"], k_new=alias, v_new=vn)
+    with pytest.raises(gq.GqaError):  # the two caches overlapping
+        gq.decode_step(x["q"], x["k_cache"], x["k_cache"], x["seqlens"], k_new=kn, v_new=vn)
