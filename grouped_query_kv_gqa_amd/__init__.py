@@ -54,11 +54,12 @@ def load_library():
     lib.gqa_decode_ex.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, i32]
     lib.gqa_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, i32, vp, vp]
     lib.gqa_prefill.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
+    lib.gqa_prefill_ex.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.gqa_mean_pool_kv.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp]
     lib.gqa_decode_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32),
                                     ctypes.POINTER(i32), ctypes.POINTER(i64)]
-    for fn in ("gqa_decode", "gqa_decode_ex", "gqa_decode_step", "gqa_prefill", "gqa_mean_pool_kv",
-               "gqa_decode_plan"):
+    for fn in ("gqa_decode", "gqa_decode_ex", "gqa_decode_step", "gqa_prefill", "gqa_prefill_ex",
+               "gqa_mean_pool_kv", "gqa_decode_plan"):
         getattr(lib, fn).restype = i32
     lib.gqa_status_string.argtypes = [i32]
     lib.gqa_status_string.restype = ctypes.c_char_p
@@ -171,8 +172,9 @@ def decode_step(q, k_cache, v_cache, seqlens, scale: float | None = None, k_new=
     return out
 
 
-def prefill(q, k, v, causal: bool = True, out=None):
-    """q [B,T,H,D]; k, v [B,T,G,D]. Returns out [B,T,H,D], scale 1/sqrt(D)."""
+def prefill(q, k, v, causal: bool = True, out=None, window: int = 0):
+    """q [B,T,H,D]; k, v [B,T,G,D]. Returns out [B,T,H,D], scale 1/sqrt(D).
+    window > 0 (causal only): query t sees keys [t + 1 - window, t]."""
     lib = load_library()
     B, T, H, D = q.shape
     if k.shape[:2] != (B, T) or k.shape[3] != D or tuple(v.shape) != tuple(k.shape):
@@ -186,8 +188,8 @@ def prefill(q, k, v, causal: bool = True, out=None):
     elif out.shape != q.shape or out.dtype != q.dtype or out.device != dev or not out.is_contiguous():
         raise ValueError("out must match q")
     with torch.cuda.device(dev):
-        _check(lib.gqa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, H, G, D, int(bool(causal)),
-                               _dtype_code(q), out.data_ptr(), _stream_ptr(dev)))
+        _check(lib.gqa_prefill_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, H, G, D, int(bool(causal)),
+                                  int(window), _dtype_code(q), out.data_ptr(), _stream_ptr(dev)))
     return out
 
 

@@ -194,22 +194,32 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, c
     return gqa_decode_ex(q, k_cache, v_cache, seqlens, B, H, G, d_h, Tmax, scale, dtype, out, stream, 0);
 }
 
-gqa_status gqa_prefill(const void *q, const void *k, const void *v, int B, int T, int H, int G, int d_h, int causal,
-                       gqa_dtype dtype, void *out, hipStream_t stream)
+gqa_status gqa_prefill_ex(const void *q, const void *k, const void *v, int B, int T, int H, int G, int d_h,
+                          int causal, int window, gqa_dtype dtype, void *out, hipStream_t stream)
 {
     std::string err;
     gqa_status s = gqa::check_prefill(q, k, v, B, T, H, G, d_h, causal, dtype, out, &err);
     if (s != GQA_OK)
         return record(s, err);
+    if (window < 0)
+        return record(GQA_ERR_INVALID_ARG, "window must be >= 0");
+    if (window > 0 && !causal)
+        return record(GQA_ERR_INVALID_ARG, "a sliding window needs causal = 1");
     if (B == 0 || T == 0)
         return GQA_OK;
     if ((int64_t)B * T * H > 0x7fffffff)
         return record(GQA_ERR_UNSUPPORTED, "B*T*H must fit in 31 bits");
-    gqa::PrefillArgs a{q, k, v, B, T, H, G, d_h, causal, out, stream};
+    gqa::PrefillArgs a{q, k, v, B, T, H, G, d_h, causal, window, out, stream};
     hipError_t e = gqa::launch_prefill(a, dtype);
     if (e != hipSuccess)
         return hip_failure(e, "prefill launch");
     return GQA_OK;
+}
+
+gqa_status gqa_prefill(const void *q, const void *k, const void *v, int B, int T, int H, int G, int d_h, int causal,
+                       gqa_dtype dtype, void *out, hipStream_t stream)
+{
+    return gqa_prefill_ex(q, k, v, B, T, H, G, d_h, causal, 0, dtype, out, stream);
 }
 
 gqa_status gqa_mean_pool_kv(const void *in, int64_t N, int H, int G, int d_h, gqa_dtype dtype, void *out,

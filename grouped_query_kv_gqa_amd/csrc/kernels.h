@@ -29,6 +29,7 @@ struct PrefillArgs {
     const void *q, *k, *v;
     int B, T, H, G, D;
     int causal;
+    int window;  // causal sliding window (0: none): query t sees keys [t + 1 - window, t]
     void *out;
     hipStream_t stream;
 };

@@ -74,7 +74,7 @@ __device__ __forceinline__ void st<__bf16>(__bf16 *p, float x)
 template <typename T, int D>
 __global__ void __launch_bounds__(64)
 prefill_row_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, int T_, int H,
-                   int G, int causal, float scale, T *__restrict__ out)
+                   int G, int causal, int window, float scale, T *__restrict__ out)
 {
     constexpr int J = D / 64;
     const int64_t row = blockIdx.x;  // ((b * T) + t) * H + h
@@ -86,6 +86,7 @@ prefill_row_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
     const int g = h / r;
     const int lane = threadIdx.x;
     const int nkeys = causal ? t + 1 : T_;
+    const int s0 = (causal && window > 0) ? max(0, t + 1 - window) : 0;  // first admissible key
     float qv[J], acc[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -93,7 +94,7 @@ prefill_row_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
         acc[j] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
-    for (int s = 0; s < nkeys; ++s) {
+    for (int s = s0; s < nkeys; ++s) {
         const int64_t off = ((b * T_ + s) * G + g) * D;
         float dot = 0.f;
 #pragma unroll
@@ -122,11 +123,11 @@ hipError_t launch_rows(const PrefillArgs &a)
     if (a.D == 64)
         prefill_row_kernel<T, 64><<<dim3((unsigned)rows), 64, 0, a.stream>>>(
             static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v), a.T, a.H, a.G,
-            a.causal, scale, static_cast<T *>(a.out));
+            a.causal, a.window, scale, static_cast<T *>(a.out));
     else
         prefill_row_kernel<T, 128><<<dim3((unsigned)rows), 64, 0, a.stream>>>(
             static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v), a.T, a.H, a.G,
-            a.causal, scale, static_cast<T *>(a.out));
+            a.causal, a.window, scale, static_cast<T *>(a.out));
     return hipGetLastError();
 }
 
@@ -186,10 +187,10 @@ __device__ __forceinline__ void buffer_rows_to_lds(const __bf16 *base, int nrec,
 // K is read one tile ahead of V, so the buffers are staggered: iteration j
 // reads K_{j+1} and V_j and loads K_{j+2} and V_{j+1} into the buffers that
 // held K_j and V_{j-1}.
-template <int D>
+template <int D, bool WIN>
 __global__ void __launch_bounds__(64 * kPfWaves, 8 / kPfWaves)
 prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16 *vp, int T, int H, int G, int r,
-                    int QT, int causal, float scale_log2, __bf16 *__restrict__ out)
+                    int QT, int causal, int window, float scale_log2, __bf16 *__restrict__ out)
 {
     using C = PfCfg<D>;
     using SW = PfSwz<D>;
@@ -225,6 +226,7 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     const bool row_ok = rho < QT * r && tq < T;
     const int64_t qrow = ((int64_t)b * T + min(tq, T - 1)) * H + g * r + rho % r;
     const int t_row_min = t0 + (wave * 32) / r;  // first query token of this wave
+    const int t_row_max = min(T - 1, t0 + min(wave * 32 + 31, QT * r - 1) / r);  // last one
 
     // Q^T as the B operand: lane holds q[row][16*ks + 8*h .. +7] times
     // c = log2(e)/sqrt(d_h), rounded to bf16, so that the MFMA yields scores
@@ -249,6 +251,14 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     const int ntiles = (kv_end + kPfBN - 1) / kPfBN;
     // Tiles below j_mask need no mask for any row of the workgroup.
     const int j_mask = causal ? t0 / kPfBN : T / kPfBN;
+    // With a sliding window (causal only), row t sees keys [t + 1 - window, t]:
+    // the workgroup starts at the first key tile any of its rows needs, and
+    // tiles below j_left may hold keys left of some row's window.
+    if constexpr (!WIN)
+        window = 0;
+    const int j_lo = WIN ? max(0, t0 + 1 - window) / kPfBN : 0;
+    const int j_left = WIN ? max(j_lo, (max(0, t_hi - window) + kPfBN - 1) / kPfBN) : 0;
+    const int nrel = ntiles - j_lo;  // tiles visited: relative tile i is key tile j_lo + i
 
     // Tile loads go straight from global memory into LDS
     // (buffer_load_dwordx4 ... lds): lane i of a wave instruction fills the
@@ -316,17 +326,19 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     // Register v of S^T tile mt holds key tile*64 + 32*mt + 8*(v/4) + 4*h + v%4.
     auto mask = [&](f32x16_t (&st)[2], int tile) {
         const int tile_last = tile * kPfBN + kPfBN - 1;
-        const bool need = causal ? (tile_last > t_row_min) : (tile_last >= T);
-        if (!need)
+        const bool need_right = causal ? (tile_last > t_row_min) : (tile_last >= T);
+        const bool need_left = WIN && tile * kPfBN < t_row_max + 1 - window;
+        if (!need_right && !need_left)
             return;
-        const int key_lim = causal ? tq : T - 1;  // last admissible key
+        const int key_lim = causal ? tq : T - 1;             // last admissible key
+        const int key_lo = WIN ? tq + 1 - window : 0;  // first admissible key
         const int tk0 = tile * kPfBN + 4 * h;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int tk = tk0 + 32 * mt + 8 * (v >> 2) + (v & 3);
-                st[mt][v] = (tk <= key_lim) ? st[mt][v] : -INFINITY;
+                st[mt][v] = (tk <= key_lim && tk >= key_lo) ? st[mt][v] : -INFINITY;
             }
     };
 
@@ -341,6 +353,7 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     constexpr float kLazy = 8.f;
     float m_run = 0.f, l_run = 0.f, alpha = 1.f;
     bool move = false;
+    bool m_set = false;  // a finite reference exists (a window may hide every key of the first tile)
     // maximum() (NaN-propagating) maps to three-input v_maximum3 without the
     // operand canonicalisation that fmaxf costs.
     auto max_part = [&](const f32x16_t (&st)[2], int v, float &mx0, float &mx1) {
@@ -351,9 +364,11 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     auto max_finish = [&](float mx0, float mx1) {
         float mx = __builtin_elementwise_maximum(mx0, mx1);
         mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32, 64));  // relative to m_run
-        move = mx > kLazy;
+        const bool first = WIN && !m_set && mx != -INFINITY;  // O and l are still zero
+        move = mx > kLazy || first;
         delta = move ? mx : 0.f;
-        alpha = fast_exp2(-delta);
+        alpha = first ? 0.f : fast_exp2(-delta);
+        m_set = m_set || first;
         m_run += delta;
     };
     auto row_max = [&](const f32x16_t (&st)[2]) {
@@ -423,9 +438,9 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         constexpr int p = decltype(P)::value;
         wait_vector_memory();  // this wave's loads of K_{j+1} and V_j have landed
         __syncthreads();       // everyone's have; every wave is done with K_j and V_{j-1}
-        if (j + 2 < ntiles)
-            load_tile(kp, kbuf(Ic<p>{}), j + 2, false);
-        load_tile(vp, vbuf(Ic<1 - p>{}), j + 1, true);
+        if (j + 2 < nrel)
+            load_tile(kp, kbuf(Ic<p>{}), j_lo + j + 2, false);
+        load_tile(vp, vbuf(Ic<1 - p>{}), j_lo + j + 1, true);
         rescale(st[p]);
         const __bf16 *Kc = kbuf(Ic<1 - p>{});
         const __bf16 *Vc = vbuf(Ic<p>{});
@@ -488,17 +503,17 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         l_run += ps0 + ps1;
         max_finish(mx0, mx1);
     };
-    // Tail iterations (the tile after them needs a mask, or none follows):
-    // plain order, buffers picked at run time, S_j kept in st[0].
+    // Plain iterations (the tile after them needs a mask, or none follows):
+    // program order, buffers picked at run time, S_j kept in st[0].
     auto tail = [&](int j) {
         const bool odd = j & 1;
         wait_vector_memory();
         __syncthreads();
-        const bool more = j + 1 < ntiles;
+        const bool more = j + 1 < nrel;
         if (more) {
-            if (j + 2 < ntiles)
-                load_tile(kp, odd ? Ks1 : Ks0, j + 2, false);
-            load_tile(vp, odd ? Vs0 : Vs1, j + 1, true);
+            if (j + 2 < nrel)
+                load_tile(kp, odd ? Ks1 : Ks0, j_lo + j + 2, false);
+            load_tile(vp, odd ? Vs0 : Vs1, j_lo + j + 1, true);
         }
         rescale(st[0]);
         u32x4_t pw[4];
@@ -514,48 +529,59 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
                                           __builtin_bit_cast(bf16x8_t, pw[s / C::DT]), acc[s % C::DT]);
         if (more) {
             qk(odd ? Ks0 : Ks1, st[0], m_run);
-            mask(st[0], j + 1);
+            mask(st[0], j_lo + j + 1);
             row_max(st[0]);
         }
     };
 
-    // Prologue: K_0, V_0 and K_1 in flight, S_0 computed.
-    load_tile(kp, Ks0, 0, false);
-    load_tile(vp, Vs0, 0, true);
-    if (ntiles > 1)
-        load_tile(kp, Ks1, 1, false);
+    // Prologue: K_0, V_0 and K_1 in flight, S_0 computed (relative tiles).
+    load_tile(kp, Ks0, j_lo, false);
+    load_tile(vp, Vs0, j_lo, true);
+    if (nrel > 1)
+        load_tile(kp, Ks1, j_lo + 1, false);
     wait_vector_memory();
     __syncthreads();
     qk(Ks0, st[0], 0.f);
-    if (j_mask <= 0)
-        mask(st[0], 0);
+    mask(st[0], j_lo);
     {
-        // The first reference is the row maximum of tile 0 (which holds at
-        // least one admissible key of every row).
+        // The first reference is the row maximum of the first tile. Without a
+        // window that tile holds key 0, admissible for every row; with one, a
+        // row may see no key of it, and its reference is set on its first
+        // admissible tile instead.
         float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
         for (int v = 0; v < 16; v += 2)
             max_part(st[0], v, mx0, mx1);
         float mx = __builtin_elementwise_maximum(mx0, mx1);
         mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32, 64));
-        m_run = (mx == -INFINITY) ? 0.f : mx;
+        m_set = mx != -INFINITY;
+        m_run = m_set ? mx : 0.f;
         st[0][0] -= m_run;
         st[0][1] -= m_run;
     }
 
-    const int n_fast = max(0, min(ntiles - 1, j_mask - 1));  // iterations whose next tile needs no mask
+    // Relative iteration j computes key tile j_lo + j + 1; the pipelined body
+    // runs while that tile needs no mask (j_left <= j_lo + j + 1 < j_mask),
+    // starting at an even j so that the buffer parity is known statically.
+    int f0 = max(0, j_left - j_lo - 1);
+    f0 += f0 & 1;
+    int f1 = min(nrel - 1, j_mask - j_lo - 1);
+    if (f1 <= f0)
+        f0 = f1 = 0;
     int j = 0;
-    for (; j + 1 < n_fast; j += 2) {
+    for (; j < f0; ++j)
+        tail(j);
+    for (; j + 1 < f1; j += 2) {
         iter(Ic<0>{}, j);
         iter(Ic<1>{}, j + 1);
     }
-    if (j < n_fast) {
+    if (j < f1) {
         iter(Ic<0>{}, j);
         ++j;
         st[0][0] = st[1][0];
         st[0][1] = st[1][1];
     }
-    for (; j < ntiles; ++j)
+    for (; j < nrel; ++j)
         tail(j);
 
     // Epilogue: lane holds O^T[dt*32 + 8*m0 + 4*h + m1][row]; 4 consecutive d per (dt, m0).
@@ -574,16 +600,16 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         }
 }
 
-template <int D>
+template <int D, bool WIN>
 hipError_t launch_mfma(const PrefillArgs &a)
 {
     const int r = a.H / a.G;
     const int QT = kPfRows / r;
     const int nqt = (a.T + QT - 1) / QT;
     const float scale_log2 = kLog2e / sqrtf((float)D);
-    prefill_bf16_kernel<D><<<dim3(nqt, a.G, a.B), 64 * kPfWaves, 0, a.stream>>>(
+    prefill_bf16_kernel<D, WIN><<<dim3(nqt, a.G, a.B), 64 * kPfWaves, 0, a.stream>>>(
         static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), static_cast<const __bf16 *>(a.v), a.T,
-        a.H, a.G, r, QT, a.causal, scale_log2, static_cast<__bf16 *>(a.out));
+        a.H, a.G, r, QT, a.causal, a.window, scale_log2, static_cast<__bf16 *>(a.out));
     return hipGetLastError();
 }
 
@@ -595,7 +621,9 @@ hipError_t launch_prefill(const PrefillArgs &a, gqa_dtype dtype)
         return launch_rows<float>(a);
     if (a.H / a.G > kPfRows)
         return launch_rows<__bf16>(a);
-    return a.D == 64 ? launch_mfma<64>(a) : launch_mfma<128>(a);
+    if (a.window > 0)
+        return a.D == 64 ? launch_mfma<64, true>(a) : launch_mfma<128, true>(a);
+    return a.D == 64 ? launch_mfma<64, false>(a) : launch_mfma<128, false>(a);
 }
 
 }  // namespace gqa

@@ -147,6 +147,20 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, int B, int T
                        int causal, gqa_dtype dtype, void *out, hipStream_t stream);
 
 /*
+ * gqa_prefill_ex -- gqa_prefill with a causal sliding window: query position
+ * t attends to key positions [max(0, t + 1 - window), t], the `window` newest
+ * ones with itself included. window = 0 is gqa_prefill.
+ * Defines: "Grouped-Query Attention" (llm-arch-kb), section 3 Reference
+ * implementation (the causal attention above) and section 4 Empirical
+ * evidence, Mistral 7B ablation (GQA paired with sliding-window attention;
+ * the window bounds above are this library's reading, the page gives none).
+ * window < 0, or window > 0 with causal = 0, is GQA_ERR_INVALID_ARG. Other
+ * arguments as for gqa_prefill.
+ */
+gqa_status gqa_prefill_ex(const void *q, const void *k, const void *v, int B, int T, int H, int G, int d_h,
+                          int causal, int window, gqa_dtype dtype, void *out, hipStream_t stream);
+
+/*
  * gqa_mean_pool_kv -- convert multi-head key or value heads into G groups by
  * averaging the r = H/G heads of each group.
  * Defines: "Grouped-Query Attention" (llm-arch-kb), section 2 Derivation,

@@ -92,3 +92,56 @@ def test_prefill_errors():
     q = torch.zeros(0, 4, 8, 128, dtype=torch.bfloat16, device=DEV)
     k = torch.zeros(0, 4, 2, 128, dtype=torch.bfloat16, device=DEV)
     assert gq.prefill(q, k, k).shape == q.shape
+
+
+WINDOW_CASES = [
+    # B, T, H, G, D, dtype
+    (2, 300, 8, 2, 128, torch.bfloat16),
+    (1, 260, 8, 8, 64, torch.bfloat16),    # MHA: 128 tokens per workgroup
+    (1, 200, 32, 1, 128, torch.bfloat16),  # r = 32: 4 tokens per workgroup
+    (2, 150, 16, 4, 64, torch.bfloat16),
+    (1, 90, 6, 3, 64, torch.float32),
+]
+
+
+@pytest.mark.parametrize("B,T,H,G,D,dtype", WINDOW_CASES)
+@pytest.mark.parametrize("window", [1, 5, 64, 100, 1000])
+def test_prefill_window_parity(B, T, H, G, D, dtype, window):
+    say(f"prefill window={window} B={B} T={T} H={H} G={G} D={D} {dtype}")
+    w = I.PrefillWorkload("win", B, T, H, G, D, dtype, True)
+    x = I.prefill_inputs(w, seed=T + window, device=DEV)
+    torch.cuda.synchronize()
+    out = gq.prefill(x["q"], x["k"], x["v"], causal=True, window=window)
+    torch.cuda.synchronize()
+    ref = O.prefill_window(to_host(x["q"]), to_host(x["k"]), to_host(x["v"]), window)
+    assert_parity(out, ref, dtype, f"window={window}")
+
+
+def test_prefill_window_full_size_sampled():
+    """Full-size causal prefill (B=4, T=8192) with a 4096-position window:
+    rows on both sides of the window edge checked one by one, and the first
+    4096 positions equal to plain causal prefill (the window covers them)."""
+    w = I.PREFILL_WORKLOADS["prefill_llama3_8b_causal"]
+    W = 4096
+    say(f"prefill {w.name} full size, window {W}")
+    x = I.prefill_inputs(w, seed=1, device=DEV)
+    out = gq.prefill(x["q"], x["k"], x["v"], causal=True, window=W)
+    full = gq.prefill(x["q"], x["k"], x["v"], causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:, :W], full[:, :W])
+    rt = np.array([W - 1, W, W + 1, 5000, 8191, 8191, 6000, 4500])
+    rb = np.array([0, 1, 2, 3, 0, 3, 1, 2])
+    rh = np.array([0, 5, 31, 8, 17, 2, 30, 9])
+    ref = O.prefill_window(to_host(x["q"]), to_host(x["k"]), to_host(x["v"]), W, rows=(rb, rt, rh))
+    got = out[torch.as_tensor(rb), torch.as_tensor(rt), torch.as_tensor(rh)]
+    assert_parity(got, ref, w.dtype, "window rows")
+
+
+def test_prefill_window_errors():
+    say("prefill window argument errors")
+    w = I.PrefillWorkload("err", 1, 16, 4, 2, 64, torch.bfloat16, True)
+    x = I.prefill_inputs(w, seed=0, device=DEV)
+    with pytest.raises(gq.GqaError):
+        gq.prefill(x["q"], x["k"], x["v"], causal=False, window=8)
+    with pytest.raises(gq.GqaError):
+        gq.prefill(x["q"], x["k"], x["v"], causal=True, window=-1)
