@@ -25,7 +25,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libgqa.so")
 
 GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_HIP = 0, 1, 2, 3
-GQA_BF16, GQA_FP32 = 0, 1
+GQA_BF16, GQA_FP32, GQA_FP16 = 0, 1, 2
 
 _lib = None
 
@@ -56,10 +56,11 @@ def load_library():
     lib.gqa_prefill.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.gqa_prefill_ex.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.gqa_mean_pool_kv.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp]
+    lib.gqa_weighted_pool_kv.argtypes = [vp, vp, i64, i32, i32, i32, i32, vp, vp]
     lib.gqa_decode_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32),
                                     ctypes.POINTER(i32), ctypes.POINTER(i64)]
     for fn in ("gqa_decode", "gqa_decode_ex", "gqa_decode_step", "gqa_prefill", "gqa_prefill_ex",
-               "gqa_mean_pool_kv", "gqa_decode_plan"):
+               "gqa_mean_pool_kv", "gqa_weighted_pool_kv", "gqa_decode_plan"):
         getattr(lib, fn).restype = i32
     lib.gqa_status_string.argtypes = [i32]
     lib.gqa_status_string.restype = ctypes.c_char_p
@@ -82,7 +83,9 @@ def _dtype_code(t: torch.Tensor) -> int:
         return GQA_BF16
     if t.dtype == torch.float32:
         return GQA_FP32
-    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+    if t.dtype == torch.float16:
+        return GQA_FP16
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16, float16 or float32")
 
 
 def _need_device(*ts: torch.Tensor):
@@ -207,11 +210,29 @@ def mean_pool_kv(x, G: int, out=None):
     return out
 
 
+def weighted_pool_kv(x, weights, G: int, out=None):
+    """x [N,H,D], weights [H] float32 on the device -> [N,G,D]: group g is
+    sum_j weights[g*r + j] * x[:, g*r + j, :] (r = H/G)."""
+    lib = load_library()
+    N, H, D = x.shape
+    if weights.dtype != torch.float32 or tuple(weights.shape) != (H,):
+        raise ValueError("weights must be float32 of shape [H]")
+    dev = _need_device(x, weights)
+    if out is None:
+        out = torch.empty((N, G, D), dtype=x.dtype, device=dev)
+    elif tuple(out.shape) != (N, G, D) or out.dtype != x.dtype or out.device != dev or not out.is_contiguous():
+        raise ValueError("out must be [N,G,D] like x")
+    with torch.cuda.device(dev):
+        _check(lib.gqa_weighted_pool_kv(x.data_ptr(), weights.data_ptr(), N, H, G, D, _dtype_code(x),
+                                        out.data_ptr(), _stream_ptr(dev)))
+    return out
+
+
 def decode_plan(B, H, G, D, Tmax, dtype=torch.bfloat16, split_tokens=0, cu_count=256):
     """(chunk_tokens, num_splits, workspace_bytes) of the decode split plan; host only."""
     lib = load_library()
     chunk, splits, ws = ctypes.c_int(), ctypes.c_int(), ctypes.c_int64()
-    code = GQA_BF16 if dtype == torch.bfloat16 else GQA_FP32
+    code = {torch.bfloat16: GQA_BF16, torch.float16: GQA_FP16}.get(dtype, GQA_FP32)
     _check(lib.gqa_decode_plan(B, H, G, D, Tmax, code, split_tokens, cu_count, ctypes.byref(chunk),
                                ctypes.byref(splits), ctypes.byref(ws)))
     return chunk.value, splits.value, ws.value

@@ -6,7 +6,8 @@
 // entry is read at a decode step; section 2 Derivation, The grouping; section
 // 3 sketch, scaled scores, softmax over keys, times v).
 //
-// bf16 design (HBM-bound: every K/V byte is read exactly once):
+// 16-bit design, bf16 or fp16 storage (HBM-bound: every K/V byte is read
+// exactly once):
 //  * Work partition. The sequences' cache positions are laid end to end
 //    (sequence b owns flat positions [pre_b, pre_b + L_b)) and cut into equal
 //    pieces of P positions, P = ceil(sum_b L_b / workgroups) rounded up to 32,
@@ -137,7 +138,7 @@ __device__ __forceinline__ Partition make_partition(const int32_t *seqlens, int 
 // APPEND: position t_new (relative to the span, or -1) is the appended token:
 // its rows come from knew_row/vnew_row (this group's slice of k_new, v_new)
 // and, when store_new, are written to the cache at that position.
-template <int D, int NT, int WPG, bool APPEND>
+template <typename T, int D, int NT, int WPG, bool APPEND>
 __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, int b, int g,
                                              int h0, int nheads, int t_off, int ta, int tb, int t_new,
                                              const __bf16 *knew_row, const __bf16 *vnew_row, bool store_new,
@@ -231,7 +232,7 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
                 f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < C::KS; ++s)
-                    c = mfma16x16x32(__builtin_bit_cast(bf16x8_t, kbuf[mt][s]), qf[nt][s], c);
+                    c = mfma16x16x32<T>(__builtin_bit_cast(bf16x8_t, kbuf[mt][s]), qf[nt][s], c);
                 st[mt][nt] = c;
             }
         if constexpr (APPEND) {
@@ -295,14 +296,14 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     st[mt][nt][i] = fast_exp2(st[mt][nt][i] - m_new);
-            pf[nt] = pack_bf16x8(st[0][nt], st[1][nt]);
+            pf[nt] = pack8<T>(st[0][nt], st[1][nt]);
             // The denominator sums the same bf16-rounded weights that enter
             // the P.V product, so the output is a convex combination of V rows.
             const u32x4_t pu = __builtin_bit_cast(u32x4_t, pf[nt]);
             float psum = 0.f;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                psum += bf16_bits_to_f32(pu[j] & 0xffffu) + bf16_bits_to_f32(pu[j] >> 16);
+                psum += bits_to_f32<T>(pu[j] & 0xffffu) + bits_to_f32<T>(pu[j] >> 16);
             l_run[nt] = l_run[nt] * alpha + psum;
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt)
@@ -318,7 +319,7 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
             const bf16x8_t vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
-                acc[nt][dt] = mfma16x16x32(vf, pf[nt], acc[nt][dt]);
+                acc[nt][dt] = mfma16x16x32<T>(vf, pf[nt], acc[nt][dt]);
         }
 
         if (tn >= tb)
@@ -344,7 +345,7 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt) {
                 const f32x4_t o = acc[nt][dt] * inv;
-                u32x2_t u = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                u32x2_t u = {pack2<T>(o[0], o[1]), pack2<T>(o[2], o[3])};
                 *reinterpret_cast<u32x2_t *>(dst + dt * 16) = u;
             }
         } else {
@@ -358,9 +359,9 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
     }
 }
 
-template <int D, int NT, int WAVES, int GB, bool APPEND>
+template <typename T, int D, int NT, int WAVES, int GB, bool APPEND>
 __global__ void __launch_bounds__(WAVES * 64)
-decode_bf16_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const __bf16 *__restrict__ knew,
+decode_split_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const __bf16 *__restrict__ knew,
                    const __bf16 *__restrict__ vnew, const int32_t *__restrict__ seqlens, int B, int H, int G,
                    int Tmax, int window, int r, int head_tiles, float scale_log2, int nwg, int fixed_P,
                    __bf16 *__restrict__ out, float *__restrict__ part, float *__restrict__ lse)
@@ -415,7 +416,7 @@ decode_bf16_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const _
             const int lo_b = __shfl(sp.lo, i, 64);
             const int t_new = (APPEND && __shfl((int)sp.appended, i, 64)) ? L - 1 : -1;
             const int64_t new_off = ((int64_t)b * G + g) * D;
-            decode_piece<D, NT, WPG, APPEND>(q, kc, vc, b, g, h0, nheads, lo_b, ta, tb, t_new, knew + new_off,
+            decode_piece<T, D, NT, WPG, APPEND>(q, kc, vc, b, g, h0, nheads, lo_b, ta, tb, t_new, knew + new_off,
                                              vnew + new_off, ht == 0, whole, H, G, Tmax, sub, scale_log2,
                                              &vlds[wave][0], out, part + slot * D, lse + slot, WPG, lane);
         }
@@ -430,7 +431,7 @@ decode_bf16_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const _
 // d-quad are combined with shuffles. out = sum_j w_j o_j with
 // w_j = 2^(lse_j - M) / sum_j' 2^(lse_j' - M). Also writes the zero rows of
 // empty sequences; rows that the decode kernel wrote whole are skipped.
-template <int D, int NQ>
+template <typename T, int D, int NQ>
 __global__ void __launch_bounds__(256)
 decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax, int append, int window, int nwg,
                     int fixed_P, int wpg, const float *__restrict__ part, const float *__restrict__ lse,
@@ -527,32 +528,32 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
     }
     if (sl == 0) {
         const float inv = 1.f / den;
-        u32x2_t u = {pack_bf16x2(num[0] * inv, num[1] * inv), pack_bf16x2(num[2] * inv, num[3] * inv)};
+        u32x2_t u = {pack2<T>(num[0] * inv, num[1] * inv), pack2<T>(num[2] * inv, num[3] * inv)};
         *reinterpret_cast<u32x2_t *>(dst) = u;
     }
 }
 
-template <int D, int NQ>
+template <typename T, int D, int NQ>
 hipError_t launch_merge(const DecodePlan &p, const DecodeArgs &a, int wpg)
 {
     constexpr int NDC = D / (4 * NQ);
     dim3 grid((unsigned)((a.H * NDC + 3) / 4), (unsigned)a.B);
-    decode_merge_kernel<D, NQ><<<grid, 256, 0, a.stream>>>(a.seqlens, a.B, a.H, a.Tmax, a.knew != nullptr,
+    decode_merge_kernel<T, D, NQ><<<grid, 256, 0, a.stream>>>(a.seqlens, a.B, a.H, a.Tmax, a.knew != nullptr,
                                                           a.window, p.nwg, p.fixed_P, wpg, a.part, a.lse,
                                                           static_cast<__bf16 *>(a.out));
     return hipGetLastError();
 }
 
-template <int D>
+template <typename T, int D>
 hipError_t launch_merge_d(const DecodePlan &p, const DecodeArgs &a, int wpg)
 {
     switch (p.merge_nq) {
-    case 1: return launch_merge<D, 1>(p, a, wpg);
-    case 2: return launch_merge<D, 2>(p, a, wpg);
-    case 4: return launch_merge<D, 4>(p, a, wpg);
-    case 8: return launch_merge<D, 8>(p, a, wpg);
-    case 16: return launch_merge<D, 16>(p, a, wpg);
-    default: return launch_merge<D, (D >= 128 ? 32 : 16)>(p, a, wpg);
+    case 1: return launch_merge<T, D, 1>(p, a, wpg);
+    case 2: return launch_merge<T, D, 2>(p, a, wpg);
+    case 4: return launch_merge<T, D, 4>(p, a, wpg);
+    case 8: return launch_merge<T, D, 8>(p, a, wpg);
+    case 16: return launch_merge<T, D, 16>(p, a, wpg);
+    default: return launch_merge<T, D, (D >= 128 ? 32 : 16)>(p, a, wpg);
     }
 }
 
@@ -612,13 +613,14 @@ decode_f32_kernel(const float *__restrict__ q, float *kc, float *vc, const float
 }
 
 template <int D, int NT, int WAVES, int GB>
-const void *bf16_symbol()
+const void *split_symbol()
 {
-    return reinterpret_cast<const void *>(&decode_bf16_kernel<D, NT, WAVES, GB, false>);
+    return reinterpret_cast<const void *>(&decode_split_kernel<__bf16, D, NT, WAVES, GB, false>);
 }
 
-template <int D, int NT, int WAVES, int GB>
-hipError_t launch_bf16(const DecodePlan &p, const DecodeArgs &a)
+// 16-bit storage of type T; the pointers carry its raw bit patterns.
+template <typename T, int D, int NT, int WAVES, int GB>
+hipError_t launch_split(const DecodePlan &p, const DecodeArgs &a)
 {
     dim3 grid(p.nwg, (a.G / GB) * p.head_tiles);
     // The caches are written only when appending (a.knew set).
@@ -627,17 +629,17 @@ hipError_t launch_bf16(const DecodePlan &p, const DecodeArgs &a)
     const __bf16 *q = static_cast<const __bf16 *>(a.q);
     const __bf16 *kn = static_cast<const __bf16 *>(a.knew), *vn = static_cast<const __bf16 *>(a.vnew);
     if (a.knew)
-        decode_bf16_kernel<D, NT, WAVES, GB, true><<<grid, WAVES * 64, 0, a.stream>>>(
+        decode_split_kernel<T, D, NT, WAVES, GB, true><<<grid, WAVES * 64, 0, a.stream>>>(
             q, kc, vc, kn, vn, a.seqlens, a.B, a.H, a.G, a.Tmax, a.window, p.r, p.head_tiles, a.scale * kLog2e,
             p.nwg, p.fixed_P, static_cast<__bf16 *>(a.out), a.part, a.lse);
     else
-        decode_bf16_kernel<D, NT, WAVES, GB, false><<<grid, WAVES * 64, 0, a.stream>>>(
+        decode_split_kernel<T, D, NT, WAVES, GB, false><<<grid, WAVES * 64, 0, a.stream>>>(
             q, kc, vc, kn, vn, a.seqlens, a.B, a.H, a.G, a.Tmax, a.window, p.r, p.head_tiles, a.scale * kLog2e,
             p.nwg, p.fixed_P, static_cast<__bf16 *>(a.out), a.part, a.lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    return launch_merge_d<D>(p, a, WAVES / GB);
+    return launch_merge_d<T, D>(p, a, WAVES / GB);
 }
 
 // Dispatch over the compiled variants: (d_h, head tiles NT, waves, groups per workgroup GB).
@@ -663,7 +665,7 @@ hipError_t with_variant(const DecodePlan &p, int D, F &&f)
 hipError_t decode_blocks_per_cu(const DecodePlan &p, int D, int *blocks)
 {
     return with_variant(p, D, [&]<int DD, int NTT, int WW, int GG>() {
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, bf16_symbol<DD, NTT, WW, GG>(), WW * 64, 0);
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, split_symbol<DD, NTT, WW, GG>(), WW * 64, 0);
     });
 }
 
@@ -684,7 +686,13 @@ hipError_t launch_decode(const DecodePlan &p, const DecodeArgs &a, gqa_dtype dty
                                                               a.window, p.r, a.scale, static_cast<float *>(a.out));
         return hipGetLastError();
     }
-    return with_variant(p, a.D, [&]<int DD, int NTT, int WW, int GG>() { return launch_bf16<DD, NTT, WW, GG>(p, a); });
+    if (dtype == GQA_FP16)
+        return with_variant(p, a.D, [&]<int DD, int NTT, int WW, int GG>() {
+            return launch_split<_Float16, DD, NTT, WW, GG>(p, a);
+        });
+    return with_variant(p, a.D, [&]<int DD, int NTT, int WW, int GG>() {
+        return launch_split<__bf16, DD, NTT, WW, GG>(p, a);
+    });
 }
 
 }  // namespace gqa

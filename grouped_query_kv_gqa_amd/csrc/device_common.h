@@ -13,57 +13,98 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 namespace gqa {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// 16x16x32 bf16 MFMA, fp32 accumulate. Lane l supplies A[l%16][8*(l/16) .. +7]
+// The 16-bit kernels are templates over the storage type T (__bf16 or
+// _Float16). Registers and LDS hold the raw 16-bit patterns in bf16x8_t /
+// bf16x4_t containers for either type; the helpers below pick the matching
+// MFMA and conversion instructions.
+template <typename T>
+inline constexpr bool kIsF16 = __is_same(T, _Float16);
+
+// 16x16x32 MFMA, fp32 accumulate. Lane l supplies A[l%16][8*(l/16) .. +7]
 // and B[8*(l/16) .. +7][l%16]; it receives C[4*(l/16) .. +3][l%16].
+template <typename T>
 __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c)
 {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    if constexpr (kIsF16<T>)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                      c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// 32x32x16 bf16 MFMA, fp32 accumulate. Lane l supplies A[l%32][8*(l/32) .. +7]
+// 32x32x16 MFMA, fp32 accumulate. Lane l supplies A[l%32][8*(l/32) .. +7]
 // and B[8*(l/32) .. +7][l%32]; register v = 4*m0 + m1 of the result holds
 // C[8*m0 + 4*(l/32) + m1][l%32].
+template <typename T>
 __device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c)
 {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    if constexpr (kIsF16<T>)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                      c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes,
 // lane i addresses 4 consecutive 16-bit elements at row i/4, columns
 // 4*(i%4) .. +3 of a 4 x 16 block; after the read lane i holds column i of
-// that block, rows 0..3.
+// that block, rows 0..3. It moves bits only, so it serves either 16-bit type.
 __device__ __forceinline__ bf16x4_t lds_read_tr16(const __bf16 *p)
 {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((GQA_LDS bf16x4_t *)(p));
 }
 
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16)
+// The value of one stored 16-bit pattern (low 16 bits of bits16).
+template <typename T>
+__device__ __forceinline__ float bits_to_f32(uint32_t bits16)
 {
-    return __uint_as_float(bits16 << 16);
+    if constexpr (kIsF16<T>)
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+    else
+        return __uint_as_float(bits16 << 16);
 }
 
-// Two floats to two bf16, round to nearest even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+// Two floats to two T, round to nearest even (v_cvt_pk_bf16_f32 /
+// v_cvt_pk_f16_f32), lo in the low half.
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi)
 {
-    bf16x2_t v = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
-    return __builtin_bit_cast(uint32_t, v);
+    if constexpr (kIsF16<T>)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
-__device__ __forceinline__ bf16x8_t pack_bf16x8(f32x4_t a, f32x4_t b)
+template <typename T>
+__device__ __forceinline__ bf16x8_t pack8(f32x4_t a, f32x4_t b)
 {
     u32x4_t u;
-    u[0] = pack_bf16x2(a[0], a[1]);
-    u[1] = pack_bf16x2(a[2], a[3]);
-    u[2] = pack_bf16x2(b[0], b[1]);
-    u[3] = pack_bf16x2(b[2], b[3]);
+    u[0] = pack2<T>(a[0], a[1]);
+    u[1] = pack2<T>(a[2], a[3]);
+    u[2] = pack2<T>(b[0], b[1]);
+    u[3] = pack2<T>(b[2], b[3]);
     return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// acc + (sum of the two T values packed in w), one dot-product instruction.
+template <typename T>
+__device__ __forceinline__ float add_pair(uint32_t w, float acc)
+{
+    if constexpr (kIsF16<T>)
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), (f16x2_t){(_Float16)1.f, (_Float16)1.f}, acc,
+                                      false);
+    else
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), (bf16x2_t){(__bf16)1.f, (__bf16)1.f},
+                                               acc, false);
 }
 
 __device__ __forceinline__ float fast_exp2(float x)

@@ -149,7 +149,7 @@ gqa_status decode_impl(const void *q, const void *k_new, const void *v_new, cons
 
     gqa::DecodeArgs a{q, k_cache, v_cache, k_new, v_new, seqlens, B, H, G, d_h, Tmax, window, scale,
                       out, nullptr, nullptr, stream};
-    if (dtype == GQA_BF16) {
+    if (dtype != GQA_FP32) {
         int bpc = 0;
         if ((s = blocks_per_cu(device, plan, d_h, &bpc)) != GQA_OK)
             return s;
@@ -231,9 +231,28 @@ gqa_status gqa_mean_pool_kv(const void *in, int64_t N, int H, int G, int d_h, gq
         return record(s, err);
     if (N == 0)
         return GQA_OK;
-    hipError_t e = gqa::launch_mean_pool(in, N, H, G, d_h, dtype, out, stream);
+    hipError_t e = gqa::launch_mean_pool(in, nullptr, N, H, G, d_h, dtype, out, stream);
     if (e != hipSuccess)
         return hip_failure(e, "mean-pool launch");
+    return GQA_OK;
+}
+
+gqa_status gqa_weighted_pool_kv(const void *in, const float *weights, int64_t N, int H, int G, int d_h,
+                                gqa_dtype dtype, void *out, hipStream_t stream)
+{
+    std::string err;
+    gqa_status s = gqa::check_mean_pool(in, N, H, G, d_h, dtype, out, &err);
+    if (s != GQA_OK)
+        return record(s, err);
+    if (N == 0)
+        return GQA_OK;
+    if (!weights || (reinterpret_cast<uintptr_t>(weights) & 3u) != 0)
+        return record(GQA_ERR_INVALID_ARG, "weights must be a non-null, 4-byte aligned fp32 array");
+    if (gqa::ranges_overlap(out, N * G * d_h * gqa::elem_size(dtype), weights, 4 * (int64_t)H))
+        return record(GQA_ERR_INVALID_ARG, "out overlaps weights");
+    hipError_t e = gqa::launch_mean_pool(in, weights, N, H, G, d_h, dtype, out, stream);
+    if (e != hipSuccess)
+        return hip_failure(e, "weighted-pool launch");
     return GQA_OK;
 }
 

@@ -36,8 +36,9 @@ struct PrefillArgs {
 
 hipError_t launch_prefill(const PrefillArgs &args, gqa_dtype dtype);
 
-hipError_t launch_mean_pool(const void *in, int64_t N, int H, int G, int D, gqa_dtype dtype, void *out,
-                            hipStream_t stream);
+// weights: fp32 [H] per-head weights, or null for the plain mean.
+hipError_t launch_mean_pool(const void *in, const float *weights, int64_t N, int H, int G, int D, gqa_dtype dtype,
+                            void *out, hipStream_t stream);
 
 hipError_t launch_fill_i32(int *p, int64_t n, int value, hipStream_t stream);
 

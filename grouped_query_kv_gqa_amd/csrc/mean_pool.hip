@@ -1,14 +1,18 @@
-// mean_pool.hip -- averaging conversion of multi-head key/value heads into G
-// groups, and a small fill kernel used by the host library.
+// mean_pool.hip -- conversion of multi-head key/value heads into G groups
+// (plain or weighted mean), and a small fill kernel used by the host library.
 //
-// out[n,g,:] = (1/r) * sum_{j<r} in[n, g*r + j, :] with r = H/G: each new
-// group starts as the mean of the original heads assigned to it
+// Mean: out[n,g,:] = (1/r) * sum_{j<r} in[n, g*r + j, :] with r = H/G: each
+// new group starts as the mean of the original heads assigned to it
 // ("Grouped-Query Attention" (llm-arch-kb), section 2 Derivation, Uptraining
 // recipe; crackai.dev paper card, How It Works).
+// Weighted: out[n,g,:] = sum_{j<r} w[g*r + j] * in[n, g*r + j, :] with
+// caller-given per-head weights (same page, section 4 Empirical evidence:
+// the weighted-grouping reproduction, which learns such weights).
 //
 // HBM-bound: every thread owns 8 consecutive d of one (n, g) output, reads the
-// group's r input heads with 16-byte (bf16) or 32-byte (fp32) loads, sums in
-// fp32 in head order and divides once by r, so G = H copies exactly.
+// group's r input heads with 16-byte (bf16, fp16) or 32-byte (fp32) loads and
+// accumulates in fp32 in head order; the mean divides once by r, so G = H
+// copies exactly.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -17,25 +21,22 @@ namespace gqa {
 namespace {
 
 template <typename T>
-struct Chunk8;
-
-template <>
-struct Chunk8<__bf16> {
-    static __device__ __forceinline__ void load(const __bf16 *p, float (&x)[8])
+struct Chunk8 {  // 16-bit storage (__bf16 or _Float16)
+    static __device__ __forceinline__ void load(const T *p, float (&x)[8])
     {
         const u32x4_t u = *reinterpret_cast<const u32x4_t *>(p);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            x[2 * j] = bf16_bits_to_f32(u[j] & 0xffffu);
-            x[2 * j + 1] = bf16_bits_to_f32(u[j] >> 16);
+            x[2 * j] = bits_to_f32<T>(u[j] & 0xffffu);
+            x[2 * j + 1] = bits_to_f32<T>(u[j] >> 16);
         }
     }
-    static __device__ __forceinline__ void store(__bf16 *p, const float (&x)[8])
+    static __device__ __forceinline__ void store(T *p, const float (&x)[8])
     {
         u32x4_t u;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            u[j] = pack_bf16x2(x[2 * j], x[2 * j + 1]);
+            u[j] = pack2<T>(x[2 * j], x[2 * j + 1]);
         *reinterpret_cast<u32x4_t *>(p) = u;
     }
 };
@@ -59,9 +60,10 @@ struct Chunk8<float> {
     }
 };
 
-template <typename T>
+template <typename T, bool WEIGHTED>
 __global__ void __launch_bounds__(256)
-mean_pool_kernel(const T *__restrict__ in, int64_t N, int H, int G, int D, T *__restrict__ out)
+mean_pool_kernel(const T *__restrict__ in, const float *__restrict__ w, int64_t N, int H, int G, int D,
+                 T *__restrict__ out)
 {
     const int r = H / G;
     const int chunks = D / 8;
@@ -76,15 +78,24 @@ mean_pool_kernel(const T *__restrict__ in, int64_t N, int H, int G, int D, T *__
         const T *src = in + (n * H + (int64_t)g * r) * D + c * 8;
         float acc[8], x[8];
         Chunk8<T>::load(src, acc);
-        for (int j = 1; j < r; ++j) {
-            Chunk8<T>::load(src + (int64_t)j * D, x);
+        if constexpr (WEIGHTED) {
+            const float w0 = w[g * r];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                acc[e] += x[e];
+                acc[e] *= w0;
         }
+        for (int j = 1; j < r; ++j) {
+            Chunk8<T>::load(src + (int64_t)j * D, x);
+            const float wj = WEIGHTED ? w[g * r + j] : 1.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            acc[e] = acc[e] / rf;
+            for (int e = 0; e < 8; ++e)
+                acc[e] = WEIGHTED ? fmaf(wj, x[e], acc[e]) : acc[e] + x[e];
+        }
+        if constexpr (!WEIGHTED) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                acc[e] = acc[e] / rf;
+        }
         Chunk8<T>::store(out + ng * D + c * 8, acc);
     }
 }
@@ -104,19 +115,29 @@ unsigned grid_for(int64_t items, int block)
     return (unsigned)(g < 1 ? 1 : g);
 }
 
+template <typename T>
+void launch_pool_t(const void *in, const float *w, int64_t N, int H, int G, int D, void *out, hipStream_t stream)
+{
+    const unsigned grid = grid_for(N * G * (D / 8), 256);
+    if (w)
+        mean_pool_kernel<T, true><<<grid, 256, 0, stream>>>(static_cast<const T *>(in), w, N, H, G, D,
+                                                            static_cast<T *>(out));
+    else
+        mean_pool_kernel<T, false><<<grid, 256, 0, stream>>>(static_cast<const T *>(in), w, N, H, G, D,
+                                                             static_cast<T *>(out));
+}
+
 }  // namespace
 
-hipError_t launch_mean_pool(const void *in, int64_t N, int H, int G, int D, gqa_dtype dtype, void *out,
-                            hipStream_t stream)
+hipError_t launch_mean_pool(const void *in, const float *weights, int64_t N, int H, int G, int D, gqa_dtype dtype,
+                            void *out, hipStream_t stream)
 {
-    const int64_t items = N * G * (D / 8);
-    const unsigned grid = grid_for(items, 256);
     if (dtype == GQA_FP32)
-        mean_pool_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float *>(in), N, H, G, D,
-                                                          static_cast<float *>(out));
+        launch_pool_t<float>(in, weights, N, H, G, D, out, stream);
+    else if (dtype == GQA_FP16)
+        launch_pool_t<_Float16>(in, weights, N, H, G, D, out, stream);
     else
-        mean_pool_kernel<__bf16><<<grid, 256, 0, stream>>>(static_cast<const __bf16 *>(in), N, H, G, D,
-                                                           static_cast<__bf16 *>(out));
+        launch_pool_t<__bf16>(in, weights, N, H, G, D, out, stream);
     return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@ int64_t round_up(int64_t a, int64_t m)
 
 bool dtype_ok(gqa_dtype dt)
 {
-    return dt == GQA_BF16 || dt == GQA_FP32;
+    return dt == GQA_BF16 || dt == GQA_FP32 || dt == GQA_FP16;
 }
 
 }  // namespace

@@ -55,7 +55,12 @@ __device__ __forceinline__ float ld<float>(const float *p)
 template <>
 __device__ __forceinline__ float ld<__bf16>(const __bf16 *p)
 {
-    return bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(p));
+    return bits_to_f32<__bf16>(*reinterpret_cast<const uint16_t *>(p));
+}
+template <>
+__device__ __forceinline__ float ld<_Float16>(const _Float16 *p)
+{
+    return (float)*p;
 }
 
 template <typename T>
@@ -68,7 +73,12 @@ __device__ __forceinline__ void st<float>(float *p, float x)
 template <>
 __device__ __forceinline__ void st<__bf16>(__bf16 *p, float x)
 {
-    *reinterpret_cast<uint16_t *>(p) = (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu);
+    *reinterpret_cast<uint16_t *>(p) = (uint16_t)(pack2<__bf16>(x, 0.f) & 0xffffu);
+}
+template <>
+__device__ __forceinline__ void st<_Float16>(_Float16 *p, float x)
+{
+    *reinterpret_cast<uint16_t *>(p) = (uint16_t)(pack2<_Float16>(x, 0.f) & 0xffffu);
 }
 
 template <typename T, int D>
@@ -187,9 +197,10 @@ __device__ __forceinline__ void buffer_rows_to_lds(const __bf16 *base, int nrec,
 // K is read one tile ahead of V, so the buffers are staggered: iteration j
 // reads K_{j+1} and V_j and loads K_{j+2} and V_{j+1} into the buffers that
 // held K_j and V_{j-1}.
-template <int D, bool WIN>
+// E: 16-bit storage type (__bf16 or _Float16); the pointers carry its raw bits.
+template <typename E, int D, bool WIN>
 __global__ void __launch_bounds__(64 * kPfWaves, 8 / kPfWaves)
-prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16 *vp, int T, int H, int G, int r,
+prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16 *vp, int T, int H, int G, int r,
                     int QT, int causal, int window, float scale_log2, __bf16 *__restrict__ out)
 {
     using C = PfCfg<D>;
@@ -240,10 +251,10 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         f32x4_t lo, hi;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            lo[i] = bf16_bits_to_f32(i & 1 ? x[i / 2] >> 16 : x[i / 2] & 0xffffu) * scale_log2;
-            hi[i] = bf16_bits_to_f32(i & 1 ? x[2 + i / 2] >> 16 : x[2 + i / 2] & 0xffffu) * scale_log2;
+            lo[i] = bits_to_f32<E>(i & 1 ? x[i / 2] >> 16 : x[i / 2] & 0xffffu) * scale_log2;
+            hi[i] = bits_to_f32<E>(i & 1 ? x[2 + i / 2] >> 16 : x[2 + i / 2] & 0xffffu) * scale_log2;
         }
-        qf[ks] = pack_bf16x8(lo, hi);
+        qf[ks] = pack8<E>(lo, hi);
     }
 
     const int t_hi = min(T, t0 + QT);
@@ -318,8 +329,8 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         st[0] = st[1] = (f32x16_t)(-m);
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-            st[0] = mfma32x32x16(kfrag(Kc, ks, 0), qf[ks], st[0]);
-            st[1] = mfma32x32x16(kfrag(Kc, ks, 1), qf[ks], st[1]);
+            st[0] = mfma32x32x16<E>(kfrag(Kc, ks, 0), qf[ks], st[0]);
+            st[1] = mfma32x32x16<E>(kfrag(Kc, ks, 1), qf[ks], st[1]);
         }
     };
 
@@ -381,17 +392,16 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
 
     // The row sum adds the bf16-rounded p that the P V product uses (dot
     // product with (1, 1)).
-    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
     // Word w (0..15) of P_j: the bf16 pair for scores st[mt][8*qh + 2*i],
     // +1 (kk = w/4 = 2*mt + qh, i = w%4), word i of pw[kk].
     auto p_word = [&](const f32x16_t (&st)[2], int w, u32x4_t (&pw)[4], float &ps0, float &ps1) {
         const int kk = w >> 2, i = w & 3, mt = kk >> 1, qh = kk & 1;
         const float e0 = fast_exp2(st[mt][8 * qh + 2 * i]);
         const float e1 = fast_exp2(st[mt][8 * qh + 2 * i + 1]);
-        const uint32_t x = pack_bf16x2(e0, e1);
+        const uint32_t x = pack2<E>(e0, e1);
         pw[kk][i] = x;
         float &ps = (w & 1) ? ps1 : ps0;
-        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x), ones, ps, false);
+        ps = add_pair<E>(x, ps);
     };
 
     f32x16_t acc[C::DT];
@@ -466,8 +476,8 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
                 kf[ks + kPfDist][0] = kfrag(Kc, ks + kPfDist, 0);
                 kf[ks + kPfDist][1] = kfrag(Kc, ks + kPfDist, 1);
             }
-            sn[0] = mfma32x32x16(kf[ks][0], qf[ks], sn[0]);
-            sn[1] = mfma32x32x16(kf[ks][1], qf[ks], sn[1]);
+            sn[0] = mfma32x32x16<E>(kf[ks][0], qf[ks], sn[0]);
+            sn[1] = mfma32x32x16<E>(kf[ks][1], qf[ks], sn[1]);
 #pragma unroll
             for (int w = qk_w0(ks); w < qk_w0(ks + 1); ++w)
                 p_word(sc, w, pw, ps0, ps1);
@@ -490,7 +500,7 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
             const int kstep = s / C::DT, dt = s % C::DT;
             if (s + kPfDist < kPvSteps)
                 vf[s + kPfDist] = vfrag(Vc, (s + kPfDist) / C::DT, (s + kPfDist) % C::DT);
-            acc[dt] = mfma32x32x16(vf[s], __builtin_bit_cast(bf16x8_t, pw[kstep]), acc[dt]);
+            acc[dt] = mfma32x32x16<E>(vf[s], __builtin_bit_cast(bf16x8_t, pw[kstep]), acc[dt]);
             if (s < 16 - kQkWords)
                 p_word(sc, kQkWords + s, pw, ps0, ps1);
             if (s >= kMaxStart && s < kMaxStart + 8)
@@ -525,7 +535,7 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         const __bf16 *Vc = odd ? Vs1 : Vs0;
 #pragma unroll
         for (int s = 0; s < kPvSteps; ++s)
-            acc[s % C::DT] = mfma32x32x16(vfrag(Vc, s / C::DT, s % C::DT),
+            acc[s % C::DT] = mfma32x32x16<E>(vfrag(Vc, s / C::DT, s % C::DT),
                                           __builtin_bit_cast(bf16x8_t, pw[s / C::DT]), acc[s % C::DT]);
         if (more) {
             qk(odd ? Ks0 : Ks1, st[0], m_run);
@@ -594,23 +604,33 @@ prefill_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
         for (int m0 = 0; m0 < 4; ++m0) {
-            u32x2_t u = {pack_bf16x2(acc[dt][4 * m0] * inv, acc[dt][4 * m0 + 1] * inv),
-                         pack_bf16x2(acc[dt][4 * m0 + 2] * inv, acc[dt][4 * m0 + 3] * inv)};
+            u32x2_t u = {pack2<E>(acc[dt][4 * m0] * inv, acc[dt][4 * m0 + 1] * inv),
+                         pack2<E>(acc[dt][4 * m0 + 2] * inv, acc[dt][4 * m0 + 3] * inv)};
             *reinterpret_cast<u32x2_t *>(dst + dt * 32 + 8 * m0) = u;
         }
 }
 
-template <int D, bool WIN>
+template <typename E, int D, bool WIN>
 hipError_t launch_mfma(const PrefillArgs &a)
 {
     const int r = a.H / a.G;
     const int QT = kPfRows / r;
     const int nqt = (a.T + QT - 1) / QT;
     const float scale_log2 = kLog2e / sqrtf((float)D);
-    prefill_bf16_kernel<D, WIN><<<dim3(nqt, a.G, a.B), 64 * kPfWaves, 0, a.stream>>>(
+    prefill_mfma_kernel<E, D, WIN><<<dim3(nqt, a.G, a.B), 64 * kPfWaves, 0, a.stream>>>(
         static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k), static_cast<const __bf16 *>(a.v), a.T,
         a.H, a.G, r, QT, a.causal, a.window, scale_log2, static_cast<__bf16 *>(a.out));
     return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_16bit(const PrefillArgs &a)
+{
+    if (a.H / a.G > kPfRows)
+        return launch_rows<E>(a);
+    if (a.window > 0)
+        return a.D == 64 ? launch_mfma<E, 64, true>(a) : launch_mfma<E, 128, true>(a);
+    return a.D == 64 ? launch_mfma<E, 64, false>(a) : launch_mfma<E, 128, false>(a);
 }
 
 }  // namespace
@@ -619,11 +639,9 @@ hipError_t launch_prefill(const PrefillArgs &a, gqa_dtype dtype)
 {
     if (dtype == GQA_FP32)
         return launch_rows<float>(a);
-    if (a.H / a.G > kPfRows)
-        return launch_rows<__bf16>(a);
-    if (a.window > 0)
-        return a.D == 64 ? launch_mfma<64, true>(a) : launch_mfma<128, true>(a);
-    return a.D == 64 ? launch_mfma<64, false>(a) : launch_mfma<128, false>(a);
+    if (dtype == GQA_FP16)
+        return launch_16bit<_Float16>(a);
+    return launch_16bit<__bf16>(a);
 }
 
 }  // namespace gqa

@@ -19,7 +19,10 @@
  *     after a call returns and never frees caller memory.
  *   - One dtype for all floating-point tensors of a call: GQA_BF16 (bf16
  *     storage, fp32 accumulation and softmax, bf16 output rounded to nearest
- *     even) or GQA_FP32 (fp32 storage and arithmetic; a debug path).
+ *     even), GQA_FP16 (the same with IEEE fp16 storage and fp16 MFMA inputs;
+ *     the pages' own cache arithmetic counts 2-byte fp16 scalars: "Grouped-Query
+ *     Attention" (llm-arch-kb), section 2 Derivation, KV-cache footprint) or
+ *     GQA_FP32 (fp32 storage and arithmetic; a debug path).
  *   - Calls are asynchronous on `stream` (0 = the null stream): they return
  *     once the work is queued. Work on one stream runs in order.
  *   - All argument checks run on the host before anything is queued. A
@@ -50,7 +53,7 @@ typedef enum gqa_status {
     GQA_ERR_HIP = 3          /* the HIP runtime failed; see gqa_last_error() */
 } gqa_status;
 
-typedef enum gqa_dtype { GQA_BF16 = 0, GQA_FP32 = 1 } gqa_dtype;
+typedef enum gqa_dtype { GQA_BF16 = 0, GQA_FP32 = 1, GQA_FP16 = 2 } gqa_dtype;
 
 /*
  * gqa_decode -- one decode step: one new query per sequence against that
@@ -190,6 +193,22 @@ gqa_status gqa_mean_pool_kv(const void *in, int64_t N, int H, int G, int d_h, gq
  */
 gqa_status gqa_decode_plan(int B, int H, int G, int d_h, int Tmax, gqa_dtype dtype, int split_tokens,
                            int cu_count, int *chunk_tokens, int *num_splits, int64_t *workspace_bytes);
+
+/*
+ * gqa_weighted_pool_kv -- the weighted variant of gqa_mean_pool_kv: each
+ * group is a weighted sum of its r heads with caller-given per-head weights,
+ * out[n,g,:] = sum_{j<r} weights[g*r + j] * in[n, g*r + j, :] (fp32
+ * accumulation in head order). weights[h] = 1/r for every head gives the
+ * mean up to rounding.
+ * Defines: "Grouped-Query Attention" (llm-arch-kb), section 4 Empirical
+ * evidence, the Chinchilla-scale reproduction (groups formed with learned
+ * per-head weights rather than the plain mean; learning them is the caller's
+ * business).
+ *   weights  [H] fp32 DEVICE memory, 4-byte aligned, not overlapping out.
+ * Other arguments, layouts and errors as for gqa_mean_pool_kv.
+ */
+gqa_status gqa_weighted_pool_kv(const void *in, const float *weights, int64_t N, int H, int G, int d_h,
+                                gqa_dtype dtype, void *out, hipStream_t stream);
 
 /* Short constant text for a status code. */
 const char *gqa_status_string(gqa_status s);

@@ -59,6 +59,9 @@ SMALL = [
     (2, 24, 4, 64, 45, [45, 32], torch.bfloat16),
     (2, 12, 3, 64, 50, [50, 17], torch.float32),
     (3, 4, 2, 128, 33, [33, 0, 5], torch.float32),
+    (3, 32, 8, 128, 300, [300, 1, 170], torch.float16),
+    (2, 64, 1, 128, 96, [96, 31], torch.float16),     # 64 heads in one group
+    (2, 8, 8, 64, 100, [65, 100], torch.float16),     # MHA
 ]
 
 
@@ -205,3 +208,16 @@ def test_decode_empty_batch_and_errors():
     with pytest.raises(gq.GqaError) as e:
         gq.decode(q, kc, kc, sl)
     assert e.value.status == gq.GQA_ERR_UNSUPPORTED
+
+
+def test_decode_llama3_8b_fp16_full():
+    """The Llama-3-8B decode layer with fp16 storage (the pages count 2-byte
+    fp16 cache scalars)."""
+    base = I.WORKLOADS["decode_llama3_8b"]
+    w = I.DecodeWorkload(base.name + "_fp16", base.B, base.H, base.G, base.D, base.Tmax, torch.float16)
+    say(f"decode {w.name} full size")
+    x = I.decode_inputs(w, seed=0, device=DEV)
+    out = _run(x, w.scale)
+    ref = O.decode(to_host(x["q"]), to_host(x["k_cache"]), to_host(x["v_cache"]), to_host(x["seqlens"]), w.scale)
+    ma, rl = assert_parity(out, ref, w.dtype, w.name)
+    print(f"{w.name}: max-abs {ma:.3e} rel-L2 {rl:.3e}")

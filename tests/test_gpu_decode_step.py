@@ -24,7 +24,7 @@ DEV = "cuda"
 
 def _bits(t):
     t = to_host(t)
-    return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+    return t.view(torch.int16).numpy().view(np.uint16) if t.dtype in (torch.bfloat16, torch.float16) else t.numpy()
 
 
 def _case(B, H, G, D, Tmax, seqlens, dtype, seed):
@@ -59,6 +59,7 @@ STEP = [
     (2, 24, 4, 64, 45, [44, 0], torch.bfloat16),
     (3, 12, 3, 64, 50, [50, 17, 0], torch.float32),
     (2, 4, 2, 128, 33, [32, 5], torch.float32),
+    (3, 32, 8, 128, 200, [199, 0, 64], torch.float16),
 ]
 
 

@@ -19,6 +19,8 @@ DEV = "cuda"
     (257, 32, 8, 64, torch.bfloat16),
     (100, 12, 3, 64, torch.float32),
     (8192, 64, 8, 128, torch.float32),   # a Llama-2-70B W_K viewed as [d, H, d_h]
+    (500, 64, 8, 128, torch.float16),
+    (129, 8, 2, 64, torch.float16),
 ])
 def test_mean_pool_parity(N, H, G, D, dtype):
     say(f"mean-pool N={N} H={H} G={G} D={D} {dtype}")
@@ -29,9 +31,11 @@ def test_mean_pool_parity(N, H, G, D, dtype):
     if dtype == torch.float32:
         assert_parity(out, ref, dtype, "mean-pool fp32")
     else:
-        # one bf16 rounding of the fp32 mean: at most half an ulp
+        # one rounding of the fp32 mean to the 16-bit type: at most half an ulp
+        # (bf16: 8 significant bits, fp16: 11; fp16 subnormals below 2^-14)
         got = out.float().cpu().double().numpy()
-        assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6)
+        rel, tiny = (2.0 ** -8, 1e-6) if dtype == torch.bfloat16 else (2.0 ** -11, 2.0 ** -24)
+        assert np.all(np.abs(got - ref) <= np.abs(ref) * rel + tiny)
 
 
 def test_mean_pool_identity_and_empty():
@@ -42,3 +46,43 @@ def test_mean_pool_identity_and_empty():
     assert gq.mean_pool_kv(e, 4).shape == (0, 4, 128)
     with pytest.raises(gq.GqaError):
         gq.mean_pool_kv(x, 5)
+
+
+@pytest.mark.parametrize("N,H,G,D,dtype", [
+    (1000, 64, 8, 128, torch.bfloat16),
+    (300, 32, 4, 64, torch.float16),
+    (100, 12, 3, 64, torch.float32),
+    (77, 8, 1, 128, torch.bfloat16),
+])
+def test_weighted_pool_parity(N, H, G, D, dtype):
+    say(f"weighted pool N={N} H={H} G={G} D={D} {dtype}")
+    x = I.mean_pool_inputs(N, H, D, dtype=dtype, seed=N + 7 * G, device=DEV)
+    w = I.random_tensor((H,), seed=H + G, dtype=torch.float32, device=DEV)
+    out = gq.weighted_pool_kv(x, w, G)
+    torch.cuda.synchronize()
+    ref = O.weighted_pool(to_host(x), G, to_host(w).double().numpy())
+    # the weighted sums reach |out| ~ 10, so the bound is relative: one
+    # rounding of the fp32 sum to the output type (half an ulp) plus the fp32
+    # accumulation error of r terms
+    got = out.float().cpu().double().numpy()
+    absum = O.weighted_pool(np.abs(to_host(x).double().numpy()), G, np.abs(to_host(w).double().numpy()))
+    rel = {torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11, torch.float32: 0.0}[dtype]
+    bound = np.abs(ref) * rel + absum * (H // G) * 2.0 ** -23 + 2.0 ** -24
+    assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) - bound))
+
+
+def test_weighted_pool_one_hot_and_mean():
+    say("weighted pool: one-hot weights copy heads, 1/r weights give the mean")
+    N, H, G, D = 64, 16, 4, 128
+    r = H // G
+    x = I.mean_pool_inputs(N, H, D, dtype=torch.bfloat16, seed=3, device=DEV)
+    for j in range(r):
+        oh = torch.zeros(H, dtype=torch.float32, device=DEV)
+        oh[j::r] = 1.0
+        assert torch.equal(gq.weighted_pool_kv(x, oh, G), x[:, j::r, :])
+    mean_w = torch.full((H,), 1.0 / r, dtype=torch.float32, device=DEV)
+    a = gq.weighted_pool_kv(x, mean_w, G).float()
+    b = gq.mean_pool_kv(x, G).float()
+    assert torch.max(torch.abs(a - b)).item() <= 2.0 ** -7 * torch.max(torch.abs(b)).item()
+    with pytest.raises(ValueError):
+        gq.weighted_pool_kv(x, mean_w.double(), G)

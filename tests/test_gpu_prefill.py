@@ -29,6 +29,9 @@ SMALL = [
     (1, 33, 24, 4, 64, torch.bfloat16),
     (2, 1, 8, 2, 128, torch.bfloat16),     # one token
     (1, 40, 6, 3, 64, torch.float32),
+    (2, 77, 8, 2, 128, torch.float16),
+    (1, 130, 16, 1, 128, torch.float16),
+    (2, 65, 4, 4, 64, torch.float16),
 ]
 
 
@@ -101,6 +104,7 @@ WINDOW_CASES = [
     (1, 200, 32, 1, 128, torch.bfloat16),  # r = 32: 4 tokens per workgroup
     (2, 150, 16, 4, 64, torch.bfloat16),
     (1, 90, 6, 3, 64, torch.float32),
+    (2, 300, 8, 2, 128, torch.float16),
 ]
 
 
@@ -145,3 +149,19 @@ def test_prefill_window_errors():
         gq.prefill(x["q"], x["k"], x["v"], causal=False, window=8)
     with pytest.raises(gq.GqaError):
         gq.prefill(x["q"], x["k"], x["v"], causal=True, window=-1)
+
+
+def test_prefill_fp16_full_size_sampled():
+    """Full-size causal prefill (B=4, T=8192) with fp16 storage: late rows
+    checked one by one against the oracle."""
+    base = I.PREFILL_WORKLOADS["prefill_llama3_8b_causal"]
+    w = I.PrefillWorkload(base.name + "_fp16", base.B, base.T, base.H, base.G, base.D, torch.float16, True)
+    say(f"prefill {w.name} full size")
+    x = I.prefill_inputs(w, seed=2, device=DEV)
+    out = _run(x, True)
+    rb = np.array([0, 1, 2, 3, 0, 2])
+    rt = np.array([8191, 8000, 4096, 5555, 1, 7777])
+    rh = np.array([0, 31, 7, 12, 3, 20])
+    ref = O.prefill(to_host(x["q"]), to_host(x["k"]), to_host(x["v"]), causal=True, rows=(rb, rt, rh))
+    got = out[torch.as_tensor(rb), torch.as_tensor(rt), torch.as_tensor(rh)]
+    assert_parity(got, ref, w.dtype, "fp16 rows")
