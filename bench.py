@@ -66,7 +66,7 @@ def measured_traffic(kind: str):
 
 
 def decode_bytes(w, seqlens) -> int:
-    e = 2 if str(w.dtype).endswith("bfloat16") else 4
+    e = 4 if str(w.dtype).endswith("float32") else 2
     L = [min(max(int(x), 0), w.Tmax) for x in seqlens]
     return sum(L) * w.G * w.D * 2 * e + 2 * w.B * w.H * w.D * e + 4 * w.B
 
@@ -150,6 +150,132 @@ def run_prefill(args):
             "mean_ms": sum(per) / len(per), "inputs": x}
 
 
+def _time_calls(fn, steps, warmup):
+    """Mean milliseconds per call: HIP events on the current stream around
+    `steps` back-to-back calls after `warmup` untimed ones."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def _hbm_entry(name, byts, ms, cfg):
+    gbs = byts / (ms * 1e-3) / 1e9
+    return {"value": round(gbs, 2), "unit": "GB/s", "ms_per_call": round(ms, 5), "config": cfg,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": int(byts)}}
+
+
+def _mfma_entry(flops, ms, cfg):
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"value": round(tf, 3), "unit": "TFLOP/s", "ms_per_call": round(ms, 4), "config": cfg,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 5),
+                         "flops_per_launch": int(flops)}}
+
+
+def run_next(args):
+    """The adjacent rows built after the hot path, each timed on its own
+    workload: fused append + decode, sliding-window decode and prefill, fp16
+    storage, weighted group pooling. Every input is resident before timing."""
+    import torch
+    import grouped_query_kv_gqa_amd as gq
+    from grouped_query_kv_gqa_amd import inputs as I
+
+    res = {}
+    # fused cache append + decode: the Llama-3-8B layer, every cache one short
+    # of full, so each call writes position 4095 and attends over 4096
+    w = I.WORKLOADS[DECODE_WORKLOAD]
+    ncopy = 4
+    xs = [I.decode_inputs(w, seed=args.seed + c, device="cuda", seqlens=[w.Tmax - 1] * w.B) for c in range(ncopy)]
+    kn = I.random_tensor((w.B, w.G, w.D), seed=args.seed + 50, dtype=w.dtype, device="cuda")
+    vn = I.random_tensor((w.B, w.G, w.D), seed=args.seed + 51, dtype=w.dtype, device="cuda")
+    outs = [torch.empty_like(x["q"]) for x in xs]
+
+    def app(i):
+        x = xs[i % ncopy]
+        gq.decode_step(x["q"], x["k_cache"], x["v_cache"], x["seqlens"], scale=w.scale, k_new=kn, v_new=vn,
+                       out=outs[i % ncopy])
+    ms = _time_calls(app, args.next_steps, 5)
+    e = 2
+    row = w.G * w.D * e
+    byts = w.B * (w.Tmax - 1) * row * 2 + w.B * row * 2 * 2 + 2 * w.B * w.H * w.D * e + 4 * w.B
+    res["decode_append"] = _hbm_entry("decode_append", byts, ms, {
+        "workload": "decode_llama3_8b, caches at 4095 of 4096, append + attend over 4096", "B": w.B, "H": w.H,
+        "G": w.G, "d_h": w.D, "dtype": "bf16"})
+    del xs, outs
+
+    # sliding-window decode: the ragged Llama-2-70B batch (B=64, lengths
+    # 1024..8192) with a 4096-position window
+    w = I.WORKLOADS["decode_llama2_70b_ragged"]
+    W = 4096
+    x = I.decode_inputs(w, seed=args.seed, device="cuda")
+    out = torch.empty_like(x["q"])
+    ms = _time_calls(lambda i: gq.decode_step(x["q"], x["k_cache"], x["v_cache"], x["seqlens"], scale=w.scale,
+                                              window=W, out=out), args.next_steps, 5)
+    seen = sum(min(min(max(int(L), 0), w.Tmax), W) for L in x["seqlens"].cpu().tolist())
+    byts = seen * w.G * w.D * 2 * 2 + 2 * w.B * w.H * w.D * 2 + 4 * w.B
+    res["decode_window"] = _hbm_entry("decode_window", byts, ms, {
+        "workload": "decode_llama2_70b_ragged with a 4096-position window", "B": w.B, "H": w.H, "G": w.G,
+        "d_h": w.D, "context": w.Tmax, "window": W, "dtype": "bf16"})
+    del x
+
+    # fp16 decode on the Llama-3-8B layer
+    base = I.WORKLOADS[DECODE_WORKLOAD]
+    w = I.DecodeWorkload(base.name + "_fp16", base.B, base.H, base.G, base.D, base.Tmax, torch.float16)
+    xs = [I.decode_inputs(w, seed=args.seed + c, device="cuda") for c in range(ncopy)]
+    outs = [torch.empty_like(x["q"]) for x in xs]
+
+    def dec16(i):
+        x = xs[i % ncopy]
+        gq.decode(x["q"], x["k_cache"], x["v_cache"], x["seqlens"], scale=w.scale, out=outs[i % ncopy])
+    ms = _time_calls(dec16, args.next_steps, 5)
+    res["decode_fp16"] = _hbm_entry("decode_fp16", decode_bytes(w, [w.Tmax] * w.B), ms, {
+        "workload": "decode_llama3_8b with fp16 storage", "B": w.B, "H": w.H, "G": w.G, "d_h": w.D,
+        "context": w.Tmax, "dtype": "fp16"})
+    del xs, outs
+
+    # prefill: sliding window 4096 (bf16) and plain causal with fp16 storage
+    pw = I.PREFILL_WORKLOADS[PREFILL_WORKLOAD]
+    x = I.prefill_inputs(pw, seed=args.seed, device="cuda")
+    out = torch.empty_like(x["q"])
+    W = 4096
+    ms = _time_calls(lambda i: gq.prefill(x["q"], x["k"], x["v"], causal=True, window=W, out=out),
+                     max(2, args.prefill_steps // 2), 1)
+    pairs = sum(min(t + 1, W) for t in range(pw.T))
+    res["prefill_window"] = _mfma_entry(4 * pw.B * pw.H * pw.D * pairs, ms, {
+        "workload": "prefill_llama3_8b_causal with a 4096-position window", "B": pw.B, "T": pw.T, "H": pw.H,
+        "G": pw.G, "d_h": pw.D, "window": W, "dtype": "bf16",
+        "flops": "4*B*H*d_h*sum_t min(t+1, window)"})
+    del x, out
+    w16 = I.PrefillWorkload(pw.name + "_fp16", pw.B, pw.T, pw.H, pw.G, pw.D, torch.float16, True)
+    x = I.prefill_inputs(w16, seed=args.seed, device="cuda")
+    out = torch.empty_like(x["q"])
+    ms = _time_calls(lambda i: gq.prefill(x["q"], x["k"], x["v"], causal=True, out=out),
+                     max(2, args.prefill_steps // 2), 1)
+    res["prefill_fp16"] = _mfma_entry(prefill_flops(w16), ms, {
+        "workload": "prefill_llama3_8b_causal with fp16 storage", "B": pw.B, "T": pw.T, "H": pw.H, "G": pw.G,
+        "d_h": pw.D, "dtype": "fp16", "peak": "fp16 dense MFMA peak equals bf16"})
+    del x, out
+
+    # weighted group pooling of a Llama-2-70B key projection viewed as [d, H, d_h]
+    N, H, G, D = 8192, 64, 8, 128
+    xin = I.mean_pool_inputs(N, H, D, dtype=torch.bfloat16, seed=args.seed, device="cuda")
+    wts = I.random_tensor((H,), seed=args.seed + 3, dtype=torch.float32, device="cuda")
+    out = torch.empty((N, G, D), dtype=torch.bfloat16, device="cuda")
+    ms = _time_calls(lambda i: gq.weighted_pool_kv(xin, wts, G, out=out), args.next_steps, 5)
+    res["weighted_pool"] = _hbm_entry("weighted_pool", N * H * D * 2 + N * G * D * 2 + 4 * H, ms, {
+        "workload": "Llama-2-70B W_K as [8192, 64, 128] -> [8192, 8, 128]", "dtype": "bf16"})
+    return res
+
+
 def cpu_baseline_decode(res, budget_s):
     """Oracle over whole sequences of the decode workload, repeated until
     about `budget_s` seconds; GB/s of algorithmic bytes."""
@@ -206,11 +332,13 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--prefill-steps", type=int, default=10)
-    ap.add_argument("--prefill-warmup", type=int, default=2)
+    ap.add_argument("--prefill-warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds per CPU-baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-next", action="store_true", help="skip the adjacent rows (append, windows, fp16, pooling)")
+    ap.add_argument("--next-steps", type=int, default=50)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device-to-device copy (for HBM counter calibration)")
     args = ap.parse_args()
@@ -256,7 +384,7 @@ def main():
         "roofline": {
             # one gqa_decode call = the split kernel + the merge kernel; the
             # HIP events bracket both (and the gap between them)
-            "kernel": "decode_bf16_kernel+decode_merge_kernel",
+            "kernel": "decode_split_kernel+decode_merge_kernel",
             "bound": "hbm",
             "achieved": round(kernel_gbs, 2),
             "peak": HBM_PEAK_GBS,
@@ -278,12 +406,14 @@ def main():
             "value": round(pf["flops"] * args.prefill_steps / pf["wall"] / 1e12, 3), "unit": "TFLOP/s",
             "steps": args.prefill_steps, "warmup": args.prefill_warmup,
             "ms_per_step": round(pf["wall"] / args.prefill_steps * 1e3, 4),
-            "roofline": {"kernel": "prefill_bf16_kernel", "bound": "mfma", "achieved": round(tflops, 3),
+            "roofline": {"kernel": "prefill_mfma_kernel", "bound": "mfma", "achieved": round(tflops, 3),
                          "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 5),
                          "traffic": measured_traffic("prefill"), "flops_per_launch": pf["flops"],
                          "launch_ms": {"mean": round(pf["mean_ms"], 4), "median": round(pf["median_ms"], 4)}},
         }
+    if not args.no_next:
+        line["next"] = run_next(args)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(dec, args.cpu_budget)
         if "prefill" in line:
