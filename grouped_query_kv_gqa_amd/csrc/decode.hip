@@ -651,8 +651,7 @@ hipError_t with_variant(const DecodePlan &p, int D, F &&f)
         return f.template operator()<DD, NTT, WW, GG>();
 #define GQA_VARIANTS(DD)                                                    \
     GQA_VARIANT(DD, 1, 8, 8) GQA_VARIANT(DD, 1, 8, 4) GQA_VARIANT(DD, 1, 8, 2) GQA_VARIANT(DD, 1, 8, 1) \
-    GQA_VARIANT(DD, 2, 4, 4) GQA_VARIANT(DD, 2, 4, 2) GQA_VARIANT(DD, 2, 4, 1)                        \
-    GQA_VARIANT(DD, 4, 4, 4) GQA_VARIANT(DD, 4, 4, 2) GQA_VARIANT(DD, 4, 4, 1)
+    GQA_VARIANT(DD, 2, 4, 4) GQA_VARIANT(DD, 2, 4, 2) GQA_VARIANT(DD, 2, 4, 1)
     GQA_VARIANTS(64)
     GQA_VARIANTS(128)
 #undef GQA_VARIANTS

@@ -15,7 +15,7 @@ namespace gqa {
 // (group blocks of gb key/value groups) x (head tiles of 16*nt query heads).
 struct DecodePlan {
     int r = 0;           // query heads per group, H / G
-    int nt = 1;          // 16-head MFMA column tiles per wave: 1, 2 or 4
+    int nt = 1;          // 16-head MFMA column tiles per wave: 1 or 2
     int head_tiles = 1;  // ceil(r / (16 * nt))
     int waves = 8;       // wavefronts per workgroup
     int gb = 1;          // key/value groups per workgroup; waves / gb waves share a group
