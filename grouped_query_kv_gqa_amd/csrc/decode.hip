@@ -65,25 +65,6 @@ __device__ __forceinline__ u32x4_t load16(const __bf16 *p)
     return *reinterpret_cast<const u32x4_t *>(p);
 }
 
-__device__ __forceinline__ int64_t wave_sum_i64(int64_t x)
-{
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        x += __shfl_xor(x, m, 64);
-    return x;
-}
-
-__device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t x, int lane)
-{
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int64_t y = __shfl_up(x, (unsigned)d, 64);
-        if (lane >= d)
-            x += y;
-    }
-    return x;
-}
-
 // The cache positions one decode step reads for a sequence: [lo, lo + n).
 // L0 = clamp(seqlens[b], 0, Tmax). With append, a sequence whose cache is not
 // full gains the new token at position L0 (read from k_new/v_new, written to
@@ -105,7 +86,8 @@ __device__ __forceinline__ Span seq_span(int32_t s, int Tmax, int append, int wi
 }
 
 // Flat-position partition shared by the decode and merge kernels (both must
-// compute identical values): total positions and the piece length P.
+// compute identical values): total positions and the piece length P. The
+// host guarantees B * Tmax < 2^31, so position counts fit in 32 bits.
 struct Partition {
     int64_t total;
     int64_t P;
@@ -114,10 +96,10 @@ struct Partition {
 __device__ __forceinline__ Partition make_partition(const int32_t *seqlens, int B, int Tmax, int append, int window,
                                                     int nwg, int fixed_P, int lane)
 {
-    int64_t tot = 0;
+    int part = 0;
     for (int i = lane; i < B; i += 64)
-        tot += seq_span(seqlens[i], Tmax, append, window).n;
-    tot = wave_sum_i64(tot);
+        part += seq_span(seqlens[i], Tmax, append, window).n;
+    const int64_t tot = wave_total(part);
     int64_t P;
     if (fixed_P > 0) {
         P = fixed_P;
@@ -392,16 +374,16 @@ decode_split_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const 
         if (b0 + lane < B)
             sp = seq_span(seqlens[b0 + lane], Tmax, APPEND, window);
         const int Lc = sp.n;
-        const int64_t incl = wave_incl_scan_i64(Lc, lane);
-        const int64_t chunk_total = __shfl(incl, 63, 64);
+        const int incl = wave_incl_scan(Lc);
+        const int64_t chunk_total = __builtin_amdgcn_readlane(incl, 63);
         if (pre + chunk_total <= lo) {
             pre += chunk_total;
             continue;
         }
         const int n = min(64, B - b0);
         for (int i = 0; i < n; ++i) {
-            const int L = __shfl(Lc, i, 64);
-            const int64_t pre_b = pre + __shfl(incl, i, 64) - L;
+            const int L = __builtin_amdgcn_readlane(Lc, i);  // i is wave-uniform
+            const int64_t pre_b = pre + __builtin_amdgcn_readlane(incl, i) - L;
             if (pre_b >= hi)
                 return;
             if (L == 0 || pre_b + L <= lo)
@@ -413,8 +395,8 @@ decode_split_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const 
             const int64_t piece = (int64_t)k + b;
             // partial layout [piece][head][sub][d], log-sum-exp [piece][head][sub]
             const int64_t slot = (piece * H + h0) * WPG + sub;
-            const int lo_b = __shfl(sp.lo, i, 64);
-            const int t_new = (APPEND && __shfl((int)sp.appended, i, 64)) ? L - 1 : -1;
+            const int lo_b = __builtin_amdgcn_readlane(sp.lo, i);
+            const int t_new = (APPEND && __builtin_amdgcn_readlane((int)sp.appended, i)) ? L - 1 : -1;
             const int64_t new_off = ((int64_t)b * G + g) * D;
             decode_piece<T, D, NT, WPG, APPEND>(q, kc, vc, b, g, h0, nheads, lo_b, ta, tb, t_new, knew + new_off,
                                              vnew + new_off, ht == 0, whole, H, G, Tmax, sub, scale_log2,
@@ -447,15 +429,15 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
         return;
 
     // partition and this sequence's first flat position (each wave on its own)
-    int64_t tot = 0, pre = 0;
+    int tot_part = 0, pre_part = 0;
     for (int i = lane; i < B; i += 64) {
         const int Li = seq_span(seqlens[i], Tmax, append, window).n;
-        tot += Li;
+        tot_part += Li;
         if (i < b)
-            pre += Li;
+            pre_part += Li;
     }
-    tot = wave_sum_i64(tot);
-    const int64_t pre_b = wave_sum_i64(pre);
+    const int64_t tot = wave_total(tot_part);
+    const int64_t pre_b = wave_total(pre_part);
     int64_t P;
     if (fixed_P > 0) {
         P = fixed_P;

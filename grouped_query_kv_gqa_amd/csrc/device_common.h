@@ -130,6 +130,28 @@ __device__ __forceinline__ float wave_sum(float x)
     return x;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (no LDS round trips): within each row of 16 lanes by shifts
+// of 1, 2, 4 and 8, then row 0's total into row 1, row 2's into row 3, and
+// lane 31's running total into rows 2 and 3. Lanes whose DPP source is
+// outside the row or whose row is masked add the `old` operand, 0.
+__device__ __forceinline__ int wave_incl_scan(int x)
+{
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+    return x;
+}
+
+// Sum over the wave, the same in every lane (wave-uniform).
+__device__ __forceinline__ int wave_total(int x)
+{
+    return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
+}
+
 __device__ __forceinline__ int clamp_len(int32_t L, int Tmax)
 {
     return L < 0 ? 0 : (L > Tmax ? Tmax : (int)L);

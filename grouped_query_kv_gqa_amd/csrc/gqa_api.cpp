@@ -132,6 +132,8 @@ gqa_status decode_impl(const void *q, const void *k_new, const void *v_new, cons
         return GQA_OK;
     if (B > 65535 || (int64_t)B * H > 0x7fffffff)
         return record(GQA_ERR_UNSUPPORTED, "B must be <= 65535");
+    if ((int64_t)B * Tmax > 0x7fffffff)
+        return record(GQA_ERR_UNSUPPORTED, "B * Tmax must be below 2^31");
 
     std::lock_guard<std::mutex> lock(g_mutex);
     int device = 0;
