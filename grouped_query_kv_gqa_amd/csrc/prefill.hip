@@ -483,9 +483,9 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
                 p_word(sc, w, pw, ps0, ps1);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x402, 48 / C::KS, 0);  // VALU incl. transcendental
+            __builtin_amdgcn_sched_group_barrier(0x402, 32 / C::KS, 0);  // VALU incl. transcendental
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x402, 48 / C::KS, 0);
+            __builtin_amdgcn_sched_group_barrier(0x402, 32 / C::KS, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
 
