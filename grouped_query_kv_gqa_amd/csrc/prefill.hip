@@ -28,7 +28,10 @@
 //    of tile j+1. K runs one tile ahead of V, so each load has a whole
 //    iteration to land.
 //  * Causal: a query tile only visits key tiles up to its last token; the
-//    heaviest tiles are launched first.
+//    heaviest tiles are launched first. Workgroups are numbered so that each
+//    XCD (workgroup i runs on XCD i % 8) takes a contiguous run of query
+//    tiles of the same (sequence, group): they read the same K/V prefix
+//    through one L2.
 //  * Softmax in base 2 against a lazily moved per-row reference (rescaling
 //    only when a row maximum grows by more than 2^8); masking only on the
 //    tiles that cross the causal diagonal or the sequence end.
@@ -225,8 +228,15 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
             return Vs1;
     };
 
-    const int qt = gridDim.x - 1 - blockIdx.x;  // heaviest causal tiles first
-    const int g = blockIdx.y, b = blockIdx.z;
+    // Workgroup i of a launch runs on XCD i % 8. Give every XCD a contiguous
+    // range of work items, so that the query tiles of one (sequence, group),
+    // which read the same K/V prefix, share an L2.
+    const int nx = gridDim.x, ny = gridDim.y;
+    const int total = nx * ny * gridDim.z;
+    const int lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+    const int item = (total % 8 == 0) ? (lin % 8) * (total / 8) + lin / 8 : lin;
+    const int qt = nx - 1 - item % nx;  // heaviest causal tiles first
+    const int g = (item / nx) % ny, b = item / (nx * ny);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, h = lane >> 5;
     const int t0 = qt * QT;
