@@ -8,11 +8,11 @@
 //
 // bf16 MFMA kernel (flash-attention style, one pass over keys with an online
 // softmax; the score matrix never leaves registers):
-//  * Workgroup = (query tile, key/value group g, sequence b). Its 128 query
-//    rows are (token, head) pairs: QT = 128 / r consecutive tokens times the r
+//  * Workgroup = (query tile, key/value group g, sequence b). Its 256 query
+//    rows are (token, head) pairs: QT = 256 / r consecutive tokens times the r
 //    heads of group g, so one K/V tile in LDS serves all heads of the group
 //    (the broadcast of the sketch costs no extra memory traffic).
-//  * 4 waves x 32 rows. Scores are computed transposed, S^T = K . Q^T, with
+//  * 8 waves x 32 rows. Scores are computed transposed, S^T = K . Q^T, with
 //    32x32x16 bf16 MFMAs (keys in M, query rows in N): the result layout (a
 //    lane holds 16 keys of one row) is directly the B operand P^T of
 //    O^T = V^T . P^T, so P stays in registers.
@@ -36,7 +36,7 @@
 //    only when a row maximum grows by more than 2^8); masking only on the
 //    tiles that cross the causal diagonal or the sequence end.
 //
-// Row kernel (fp32 path, and groups of more than 128 query heads): one
+// Row kernel (fp32 path, and groups of more than 256 query heads): one
 // wavefront per (b, t, h) row, lanes split d_h, online softmax over the keys
 // one position at a time, fp32 arithmetic.
 #include <type_traits>
@@ -145,7 +145,7 @@ hipError_t launch_rows(const PrefillArgs &a)
 }
 
 constexpr int kPfBN = 64;    // key/value positions per tile
-constexpr int kPfWaves = 4;             // waves per workgroup, 32 query rows each
+constexpr int kPfWaves = 8;             // waves per workgroup, 32 query rows each
 constexpr int kPfRows = 32 * kPfWaves;  // query rows per workgroup
 
 template <int D>
