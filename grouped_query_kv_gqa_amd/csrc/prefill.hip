@@ -161,12 +161,16 @@ struct PfCfg {
 // LDS tile layout: rows of d_h elements without padding; the 16-byte chunk c
 // of row r sits at chunk slot c ^ kswz(r) (K) or c ^ vswz(r) (V). K is read
 // 16 rows at a time at one chunk (b128 reads): r mod 16 spreads them over 16
-// slots. V is read by the transposing loads 4 rows x 2 chunks at a time:
-// 2*(r mod 4) spreads those over 8 slots.
+// slots. V is read by the transposing loads, whose 32-lane halves take 4
+// rows x 4 chunks (64 bytes per row) at once: with 256-byte rows (d_h = 128)
+// vswz = 4*(r mod 4) puts the 4 rows in 4 different 64-byte bank ranges (with
+// 2*(r mod 4), measured, half of all V-read cycles were bank conflicts); with
+// 128-byte rows (d_h = 64) consecutive rows already alternate bank halves and
+// vswz = 2*(r mod 4) separates the rest.
 template <int D>
 struct PfSwz {
     static __device__ __forceinline__ int k(int r) { return r & (D / 8 - 1); }
-    static __device__ __forceinline__ int v(int r) { return (r & 3) << 1; }
+    static __device__ __forceinline__ int v(int r) { return D >= 128 ? (r & 3) << 2 : (r & 3) << 1; }
 };
 
 __device__ __forceinline__ u32x4_t ld16(const __bf16 *p)
