@@ -65,6 +65,21 @@ __device__ __forceinline__ u32x4_t load16(const __bf16 *p)
     return *reinterpret_cast<const u32x4_t *>(p);
 }
 
+// Cache rows read once per call go through nontemporal loads (streaming
+// cache policy): measured 5.9 -> 6.6 TB/s for a plain 256 MiB read on this
+// chip, and 6-7% off every decode workload with one 16-head tile per group.
+// Wider groups (two head tiles, or more head tiles that read the same rows
+// from another workgroup) keep the default policy: measured, streaming loads
+// made them up to 22% slower.
+template <bool STREAM>
+__device__ __forceinline__ u32x4_t load16_kv(const __bf16 *p)
+{
+    if constexpr (STREAM)
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    else
+        return *reinterpret_cast<const u32x4_t *>(p);
+}
+
 // The cache positions one decode step reads for a sequence: [lo, lo + n).
 // L0 = clamp(seqlens[b], 0, Tmax). With append, a sequence whose cache is not
 // full gains the new token at position L0 (read from k_new/v_new, written to
@@ -175,7 +190,7 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
                 src = (t == t_new) ? knew_row : src;
 #pragma unroll
             for (int s = 0; s < C::KS; ++s)
-                kr[mt][s] = load16(src + (s * 4 + kb) * 8);
+                kr[mt][s] = load16_kv<NT == 1>(src + (s * 4 + kb) * 8);
         }
     };
     auto load_v = [&](int t0, u32x4_t (&vr)[C::VLOADS]) {
@@ -185,7 +200,7 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
             const __bf16 *src = vbase + t * tok_stride;
             if constexpr (APPEND)
                 src = (t == t_new) ? vnew_row : src;
-            vr[i] = load16(src + (lane % C::CH) * 8);
+            vr[i] = load16_kv<NT == 1>(src + (lane % C::CH) * 8);
         }
     };
 
