@@ -411,7 +411,12 @@ decode_split_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const 
             // partial layout [piece][head][sub][d], log-sum-exp [piece][head][sub]
             const int64_t slot = (piece * H + h0) * WPG + sub;
             const int lo_b = __builtin_amdgcn_readlane(sp.lo, i);
-            const int t_new = (APPEND && __builtin_amdgcn_readlane((int)sp.appended, i)) ? L - 1 : -1;
+            // The appended token is the span's last position, so only the piece
+            // that ends there holds it. An earlier piece's last tile can reach
+            // past the piece end onto that position with clamped (older) rows
+            // in its lanes, and must neither select nor store the new row.
+            const int t_new =
+                (APPEND && __builtin_amdgcn_readlane((int)sp.appended, i) && tb == L) ? L - 1 : -1;
             const int64_t new_off = ((int64_t)b * G + g) * D;
             decode_piece<T, D, NT, WPG, APPEND>(q, kc, vc, b, g, h0, nheads, lo_b, ta, tb, t_new, knew + new_off,
                                              vnew + new_off, ht == 0, whole, H, G, Tmax, sub, scale_log2,

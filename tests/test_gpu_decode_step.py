@@ -80,6 +80,27 @@ def test_decode_window_parity(B, H, G, D, Tmax, seqlens, dtype, window):
     _check(w, x, kn, vn, window, 0, append=True)
 
 
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("B,H,G,D,Tmax,seqlens,split", [
+    # flat positions 0..97: the last sequence's span [92, 98) is cut at 96,
+    # and the tile of its first piece reaches the appended position 5
+    (3, 32, 8, 64, 47, [44, 47, 5], 0),
+    (3, 40, 5, 128, 47, [44, 47, 5], 0),
+    # caller-fixed slices of 32: the second sequence's span (flat [31, 42)) is
+    # cut at 32, and its one-position first piece's tile covers position 10
+    (2, 16, 4, 128, 64, [30, 10], 32),
+])
+def test_decode_append_split_before_new_token(B, H, G, D, Tmax, seqlens, split, dtype):
+    """Only the piece that ends at the appended position may store it: an
+    earlier piece whose last tile reaches that position holds clamped rows
+    there (regression test: they once overwrote the new row)."""
+    say(f"append with a slice boundary just before the new token B={B} H={H} G={G} D={D} {seqlens} split={split}")
+    w, x, kn, vn = _case(B, H, G, D, Tmax, seqlens, dtype, 106)
+    for _ in range(3):  # the stale store raced with the right one
+        ww, xx = w, {k: v.clone() for k, v in x.items()}
+        _check(ww, xx, kn, vn, 0, split)
+
+
 def test_decode_step_plain_matches_decode():
     w = I.DecodeWorkload("plain", 3, 32, 8, 128, 700, torch.bfloat16)
     say("decode_step without append or window equals gqa_decode")
