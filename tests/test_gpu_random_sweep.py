@@ -1,7 +1,9 @@
 """Seeded random sweep of the HIP path against the fp64 oracle.
 
 Fixed-seed draws of shapes, dtypes and options that the hand-picked parity
-cases do not line up on purpose: head/group layouts (MHA, MQA, odd group
+cases do not line up on purpose (plus a few larger draws, caches of 1000 to
+4000 positions over up to 24 sequences and prompts of 400 to 1100 tokens, so
+that sequences fall into many pieces): head/group layouts (MHA, MQA, odd group
 sizes), d_h 64 and 128, cache lengths around and away from tile edges,
 lengths out of range, appends into full and non-full caches, windows shorter
 and longer than the span, caller-fixed split lengths, causal and full
@@ -27,15 +29,15 @@ LAYOUTS = [(8, 8), (8, 2), (16, 4), (32, 8), (64, 8), (64, 1), (24, 3), (12, 6),
 DTYPES = [torch.bfloat16, torch.float16, torch.float32]
 
 
-def _decode_cases(n, seed=2024):
+def _decode_cases(n, seed=2024, big=False):
     rng = random.Random(seed)
     cases = []
     for i in range(n):
         H, G = rng.choice(LAYOUTS)
         D = rng.choice([64, 128])
-        dtype = rng.choice(DTYPES)
-        B = rng.randint(1, 6)
-        Tmax = rng.randint(1, 300 if dtype == torch.float32 else 700)
+        dtype = rng.choice(DTYPES[:2] if big else DTYPES)
+        B = rng.randint(4, 24) if big else rng.randint(1, 6)
+        Tmax = rng.randint(1000, 4000) if big else rng.randint(1, 300 if dtype == torch.float32 else 700)
         seqlens = []
         for _ in range(B):
             kind = rng.random()
@@ -56,15 +58,15 @@ def _decode_cases(n, seed=2024):
     return cases
 
 
-def _prefill_cases(n, seed=4096):
+def _prefill_cases(n, seed=4096, big=False):
     rng = random.Random(seed)
     cases = []
     for i in range(n):
         H, G = rng.choice(LAYOUTS)
         D = rng.choice([64, 128])
-        dtype = rng.choice(DTYPES)
+        dtype = rng.choice(DTYPES[:2] if big else DTYPES)
         B = rng.randint(1, 2)
-        T = rng.randint(1, 120 if dtype == torch.float32 else 333)
+        T = rng.randint(400, 1100) if big else rng.randint(1, 120 if dtype == torch.float32 else 333)
         causal = rng.random() < 0.7
         window = rng.randint(1, T + 3) if causal and rng.random() < 0.5 else 0
         cases.append((i, B, T, H, G, D, dtype, causal, window))
@@ -76,7 +78,8 @@ def _bits(t):
     return t.view(torch.int16).numpy().view(np.uint16) if t.dtype in (torch.bfloat16, torch.float16) else t.numpy()
 
 
-@pytest.mark.parametrize("case", _decode_cases(40), ids=lambda c: f"d{c[0]}")
+@pytest.mark.parametrize("case", _decode_cases(40) + [(100 + c[0],) + c[1:] for c in _decode_cases(12, 77, True)],
+                         ids=lambda c: f"d{c[0]}")
 def test_random_decode_step(case):
     i, B, H, G, D, Tmax, seqlens, dtype, append, window, split = case
     say(f"random decode #{i}: B={B} H={H} G={G} D={D} Tmax={Tmax} seqlens={list(seqlens)} {dtype} "
@@ -98,7 +101,8 @@ def test_random_decode_step(case):
         "cache contents after the call"
 
 
-@pytest.mark.parametrize("case", _prefill_cases(24), ids=lambda c: f"p{c[0]}")
+@pytest.mark.parametrize("case", _prefill_cases(24) + [(100 + c[0],) + c[1:] for c in _prefill_cases(6, 99, True)],
+                         ids=lambda c: f"p{c[0]}")
 def test_random_prefill(case):
     i, B, T, H, G, D, dtype, causal, window = case
     say(f"random prefill #{i}: B={B} T={T} H={H} G={G} D={D} {dtype} causal={causal} window={window}")
