@@ -253,22 +253,19 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     const int t_row_min = t0 + (wave * 32) / r;  // first query token of this wave
     const int t_row_max = min(T - 1, t0 + min(wave * 32 + 31, QT * r - 1) / r);  // last one
 
-    // Q^T as the B operand: lane holds q[row][16*ks + 8*h .. +7] times
-    // c = log2(e)/sqrt(d_h), rounded to bf16, so that the MFMA yields scores
-    // in base-2 units.
+    // Q^T as the B operand, exactly as stored: lane holds q[row][16*ks + 8*h
+    // .. +7]. The scale is applied to the fp32 scores (folded into the
+    // exponent's argument), never to q: rounding q*c to 16 bits would put a
+    // relative error of 2^-9 on every score, which large scores (queries
+    // scaled by 16, as outlier features can be) turn into errors of 0.1 in
+    // the output.
     bf16x8_t qf[C::KS];
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
         u32x4_t x = {0, 0, 0, 0};
         if (row_ok)
             x = ld16(q + qrow * D + ks * 16 + h * 8);
-        f32x4_t lo, hi;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            lo[i] = bits_to_f32<E>(i & 1 ? x[i / 2] >> 16 : x[i / 2] & 0xffffu) * scale_log2;
-            hi[i] = bits_to_f32<E>(i & 1 ? x[2 + i / 2] >> 16 : x[2 + i / 2] & 0xffffu) * scale_log2;
-        }
-        qf[ks] = pack8<E>(lo, hi);
+        qf[ks] = __builtin_bit_cast(bf16x8_t, x);
     }
 
     const int t_hi = min(T, t0 + QT);
@@ -337,10 +334,9 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
 
-    // S^T = K Q^T - m for one tile (plain order): two 32-key M tiles, the
-    // accumulators starting at -m.
-    auto qk = [&](const __bf16 *Kc, f32x16_t (&st)[2], float m) {
-        st[0] = st[1] = (f32x16_t)(-m);
+    // S^T = K Q^T for one tile (plain order): two 32-key M tiles.
+    auto qk = [&](const __bf16 *Kc, f32x16_t (&st)[2]) {
+        st[0] = st[1] = (f32x16_t){};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
             st[0] = mfma32x32x16<E>(kfrag(Kc, ks, 0), qf[ks], st[0]);
@@ -368,13 +364,13 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     };
 
     // Online softmax in base 2 with a lazily moved reference m_run (in
-    // scaled units): p = 2^(s*c - m_run) with c = scale*log2(e). The score
-    // MFMAs start from -m_run, so registers hold x = s*c - m_run and p =
-    // 2^x. The reference only moves when a row maximum exceeds it by more
+    // scaled units): registers hold the raw scores s (fp32) and p =
+    // 2^(s*c - m_run) with c = scale*log2(e), one FMA and one exponential per
+    // score. The reference only moves when a row maximum exceeds it by more
     // than kLazy, so p <= 2^kLazy; softmax is unchanged by the choice of
-    // reference. A move by delta found on tile j+1 subtracts delta from its
-    // scores and rescales O and l by 2^-delta at the start of the next
-    // iteration, after P_j V_j has been added.
+    // reference. A move by delta found on tile j+1 applies to the
+    // probabilities of tile j+1 on, and rescales O and l by 2^-delta at the
+    // start of the next iteration, after P_j V_j has been added.
     constexpr float kLazy = 8.f;
     float m_run = 0.f, l_run = 0.f, alpha = 1.f;
     bool move = false;
@@ -388,7 +384,8 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     float delta = 0.f;
     auto max_finish = [&](float mx0, float mx1) {
         float mx = __builtin_elementwise_maximum(mx0, mx1);
-        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32, 64));  // relative to m_run
+        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32, 64));
+        mx = fmaf(mx, scale_log2, -m_run);  // scaled, relative to m_run (-inf stays -inf)
         const bool first = WIN && !m_set && mx != -INFINITY;  // O and l are still zero
         move = mx > kLazy || first;
         delta = move ? mx : 0.f;
@@ -410,8 +407,8 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     // +1 (kk = w/4 = 2*mt + qh, i = w%4), word i of pw[kk].
     auto p_word = [&](const f32x16_t (&st)[2], int w, u32x4_t (&pw)[4], float &ps0, float &ps1) {
         const int kk = w >> 2, i = w & 3, mt = kk >> 1, qh = kk & 1;
-        const float e0 = fast_exp2(st[mt][8 * qh + 2 * i]);
-        const float e1 = fast_exp2(st[mt][8 * qh + 2 * i + 1]);
+        const float e0 = fast_exp2(fmaf(st[mt][8 * qh + 2 * i], scale_log2, -m_run));
+        const float e1 = fast_exp2(fmaf(st[mt][8 * qh + 2 * i + 1], scale_log2, -m_run));
         const uint32_t x = pack2<E>(e0, e1);
         pw[kk][i] = x;
         float &ps = (w & 1) ? ps1 : ps0;
@@ -423,14 +420,12 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     for (int dt = 0; dt < C::DT; ++dt)
         acc[dt] = (f32x16_t){};
 
-    auto rescale = [&](f32x16_t (&sc)[2]) {
+    auto rescale = [&]() {
         if (__any(move)) {
             l_run *= alpha;
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt)
                 acc[dt] *= alpha;
-            sc[0] -= delta;
-            sc[1] -= delta;
         }
     };
 
@@ -467,7 +462,7 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         if (j + 2 < nrel)
             load_tile(kp, kbuf(Ic<p>{}), j_lo + j + 2, false);
         load_tile(vp, vbuf(Ic<1 - p>{}), j_lo + j + 1, true);
-        rescale(st[p]);
+        rescale();
         const __bf16 *Kc = kbuf(Ic<1 - p>{});
         const __bf16 *Vc = vbuf(Ic<p>{});
         f32x16_t(&sc)[2] = st[p];
@@ -484,7 +479,7 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
             kf[i][0] = kfrag(Kc, i, 0);
             kf[i][1] = kfrag(Kc, i, 1);
         }
-        sn[0] = sn[1] = (f32x16_t)(-m_run);
+        sn[0] = sn[1] = (f32x16_t){};
         __builtin_amdgcn_sched_barrier(0);
         // The QK steps carry most of the exponentials: when both waves of a
         // SIMD compete for issue, the one in its QK steps goes first
@@ -557,7 +552,7 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
                 load_tile(kp, odd ? Ks1 : Ks0, j_lo + j + 2, false);
             load_tile(vp, odd ? Vs0 : Vs1, j_lo + j + 1, true);
         }
-        rescale(st[0]);
+        rescale();
         u32x4_t pw[4];
         float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
@@ -570,7 +565,7 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
             acc[s % C::DT] = mfma32x32x16<E>(vfrag(Vc, s / C::DT, s % C::DT),
                                           __builtin_bit_cast(bf16x8_t, pw[s / C::DT]), acc[s % C::DT]);
         if (more) {
-            qk(odd ? Ks0 : Ks1, st[0], m_run);
+            qk(odd ? Ks0 : Ks1, st[0]);
             mask(st[0], j_lo + j + 1);
             row_max(st[0]);
         }
@@ -583,7 +578,7 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         load_tile(kp, Ks1, j_lo + 1, false);
     wait_vector_memory();
     __syncthreads();
-    qk(Ks0, st[0], 0.f);
+    qk(Ks0, st[0]);
     mask(st[0], j_lo);
     {
         // The first reference is the row maximum of the first tile. Without a
@@ -597,9 +592,7 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         float mx = __builtin_elementwise_maximum(mx0, mx1);
         mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32, 64));
         m_set = mx != -INFINITY;
-        m_run = m_set ? mx : 0.f;
-        st[0][0] -= m_run;
-        st[0][1] -= m_run;
+        m_run = m_set ? mx * scale_log2 : 0.f;
     }
 
     // Relative iteration j computes key tile j_lo + j + 1; the pipelined body
