@@ -144,3 +144,40 @@ def test_random_pool(i):
     rel = {torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11, torch.float32: 0.0}[dtype]
     bound = np.abs(ref) * rel + absum * (H // G) * 2.0 ** -23 + 2.0 ** -24
     assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) - bound))
+
+
+@pytest.mark.parametrize("case", _prefill_cases(10, seed=555) + [(200 + c[0],) + c[1:] for c in _prefill_cases(2, 556, True)],
+                         ids=lambda c: f"q{c[0]}")
+def test_random_prefill_large_scores(case):
+    """Queries scaled by 8-16 (scores of tens of units, as outlier features
+    give): the scale must reach the scores in fp32. (Rounding q*scale to 16
+    bits once exceeded the bound here by up to 7x.)"""
+    i, B, T, H, G, D, dtype, causal, window = case
+    mult = random.Random(7000 + i).choice([8.0, 16.0])
+    say(f"large-score prefill #{i}: B={B} T={T} H={H} G={G} D={D} {dtype} causal={causal} window={window} q*{mult}")
+    w = I.PrefillWorkload("rand", B, T, H, G, D, dtype, causal)
+    x = I.prefill_inputs(w, seed=500 + i, device=DEV)
+    x["q"] = (x["q"].float() * mult).to(dtype)
+    torch.cuda.synchronize()
+    out = gq.prefill(x["q"], x["k"], x["v"], causal=causal, window=window)
+    torch.cuda.synchronize()
+    qh, kh, vh = to_host(x["q"]), to_host(x["k"]), to_host(x["v"])
+    ref = O.prefill_window(qh, kh, vh, window) if window > 0 else O.prefill(qh, kh, vh, causal=causal)
+    assert_parity(out, ref, dtype, f"large-score prefill #{i}")
+
+
+@pytest.mark.parametrize("case", _decode_cases(8, seed=556), ids=lambda c: f"e{c[0]}")
+def test_random_decode_large_scores(case):
+    i, B, H, G, D, Tmax, seqlens, dtype, append, window, split = case
+    mult = random.Random(7100 + i).choice([8.0, 16.0])
+    say(f"large-score decode #{i}: B={B} H={H} G={G} D={D} Tmax={Tmax} {dtype} window={window} q*{mult}")
+    w = I.DecodeWorkload("rand", B, H, G, D, Tmax, dtype)
+    x = I.decode_inputs(w, seed=100 + i, device=DEV, seqlens=list(seqlens))
+    x["q"] = (x["q"].float() * mult).to(dtype)
+    ref, _, _ = O.decode_step(to_host(x["q"]), to_host(x["k_cache"]), to_host(x["v_cache"]), to_host(x["seqlens"]),
+                              w.scale, window=window)
+    torch.cuda.synchronize()
+    out = gq.decode_step(x["q"], x["k_cache"], x["v_cache"], x["seqlens"], scale=w.scale, window=window,
+                         split_tokens=split)
+    torch.cuda.synchronize()
+    assert_parity(out, ref, dtype, f"large-score decode #{i}")
