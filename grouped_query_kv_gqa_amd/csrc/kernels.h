@@ -40,6 +40,4 @@ hipError_t launch_prefill(const PrefillArgs &args, gqa_dtype dtype);
 hipError_t launch_mean_pool(const void *in, const float *weights, int64_t N, int H, int G, int D, gqa_dtype dtype,
                             void *out, hipStream_t stream);
 
-hipError_t launch_fill_i32(int *p, int64_t n, int value, hipStream_t stream);
-
 }  // namespace gqa

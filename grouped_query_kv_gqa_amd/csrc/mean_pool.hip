@@ -1,5 +1,5 @@
 // mean_pool.hip -- conversion of multi-head key/value heads into G groups
-// (plain or weighted mean), and a small fill kernel used by the host library.
+// (plain or weighted mean).
 //
 // Mean: out[n,g,:] = (1/r) * sum_{j<r} in[n, g*r + j, :] with r = H/G: each
 // new group starts as the mean of the original heads assigned to it
@@ -101,12 +101,6 @@ mean_pool_kernel(const T *__restrict__ in, const float *__restrict__ w, int64_t 
     }
 }
 
-__global__ void fill_i32_kernel(int *p, int64_t n, int value)
-{
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = value;
-}
-
 unsigned grid_for(int64_t items, int block)
 {
     int64_t g = (items + block - 1) / block;
@@ -139,14 +133,6 @@ hipError_t launch_mean_pool(const void *in, const float *weights, int64_t N, int
         launch_pool_t<_Float16>(in, weights, N, H, G, D, out, stream);
     else
         launch_pool_t<__bf16>(in, weights, N, H, G, D, out, stream);
-    return hipGetLastError();
-}
-
-hipError_t launch_fill_i32(int *p, int64_t n, int value, hipStream_t stream)
-{
-    if (n <= 0)
-        return hipSuccess;
-    fill_i32_kernel<<<grid_for(n, 256), 256, 0, stream>>>(p, n, value);
     return hipGetLastError();
 }
 

@@ -1,0 +1,82 @@
+"""Streams and graph capture: libgqa queues its kernels on the caller's
+stream and keeps one split-decode workspace per (device, stream).
+
+- Decode calls of different shapes on two streams, overlapping in time, give
+  bit for bit the results of the same calls made one after the other (decode
+  is deterministic), so neither stream's partial rows leak into the other's.
+- A decode call and a prefill call captured into a HIP graph (after a
+  warm-up call on the capture stream, which sizes the workspace outside the
+  capture) and replayed with new inputs copied into the captured tensors give
+  the eager results on every replay, with eager work and synchronisation
+  between the replays.
+"""
+import pytest
+import torch
+
+import grouped_query_kv_gqa_amd as gq
+from grouped_query_kv_gqa_amd import inputs as I
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _decode(x, w):
+    return gq.decode(x["q"], x["k_cache"], x["v_cache"], x["seqlens"], scale=w.scale)
+
+
+def test_decode_two_streams_match_serial():
+    say("decode on two concurrent streams")
+    wa = I.DecodeWorkload("a", 16, 32, 8, 128, 2048, torch.bfloat16)
+    wb = I.DecodeWorkload("b", 5, 64, 8, 128, 3000, torch.bfloat16, ragged=(1, 3000))
+    xa = I.decode_inputs(wa, seed=11, device=DEV)
+    xb = I.decode_inputs(wb, seed=12, device=DEV)
+    ref_a = _decode(xa, wa).clone()
+    ref_b = _decode(xb, wb).clone()
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(4):
+        with torch.cuda.stream(sa):
+            oa = _decode(xa, wa)
+        with torch.cuda.stream(sb):
+            ob = _decode(xb, wb)
+        outs.append((oa, ob))
+    torch.cuda.synchronize()
+    for oa, ob in outs:
+        assert torch.equal(oa, ref_a)
+        assert torch.equal(ob, ref_b)
+
+
+def test_graph_capture_decode_and_prefill():
+    say("decode and prefill captured in a HIP graph, replayed with new inputs")
+    w = I.DecodeWorkload("g", 8, 32, 8, 128, 1500, torch.bfloat16, ragged=(1, 1500))
+    pw = I.PrefillWorkload("g", 1, 300, 16, 4, 128, torch.bfloat16, True)
+    x = I.decode_inputs(w, seed=21, device=DEV)
+    px = I.prefill_inputs(pw, seed=22, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up on the capture stream: the workspace exists before capture
+        _decode(x, w)
+        gq.prefill(px["q"], px["k"], px["v"], causal=True)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        out = _decode(x, w)
+        pout = gq.prefill(px["q"], px["k"], px["v"], causal=True)
+    for rep in range(3):
+        nx = I.decode_inputs(w, seed=30 + rep, device=DEV)
+        npx = I.prefill_inputs(pw, seed=40 + rep, device=DEV)
+        for key in ("q", "k_cache", "v_cache", "seqlens"):
+            x[key].copy_(nx[key])
+        for key in ("q", "k", "v"):
+            px[key].copy_(npx[key])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = _decode(nx, w)
+        pref = gq.prefill(npx["q"], npx["k"], npx["v"], causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"decode replay {rep}"
+        assert torch.equal(pout, pref), f"prefill replay {rep}"
