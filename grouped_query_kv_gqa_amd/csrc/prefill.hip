@@ -6,8 +6,8 @@
 // implementation: broadcast of each key/value head to its H/G query heads,
 // scores over sqrt(d_h), causal mask, softmax over keys, times v).
 //
-// bf16 MFMA kernel (flash-attention style, one pass over keys with an online
-// softmax; the score matrix never leaves registers):
+// 16-bit MFMA kernel, bf16 or fp16 storage (flash-attention style, one pass
+// over keys with an online softmax; the score matrix never leaves registers):
 //  * Workgroup = (query tile, key/value group g, sequence b). Its 256 query
 //    rows are (token, head) pairs: QT = 256 / r consecutive tokens times the r
 //    heads of group g, so one K/V tile in LDS serves all heads of the group
@@ -33,8 +33,10 @@
 //    tiles of the same (sequence, group): they read the same K/V prefix
 //    through one L2.
 //  * Softmax in base 2 against a lazily moved per-row reference (rescaling
-//    only when a row maximum grows by more than 2^8); masking only on the
-//    tiles that cross the causal diagonal or the sequence end.
+//    only when a row maximum grows by more than 2^8): p = 2^(s*c - m) from
+//    the fp32 score s with c = log2(e)/sqrt(d_h), one FMA per score (q is
+//    never scaled in 16 bits); masking only on the tiles that cross the
+//    causal diagonal, a window edge or the sequence end.
 //
 // Row kernel (fp32 path, and groups of more than 256 query heads): one
 // wavefront per (b, t, h) row, lanes split d_h, online softmax over the keys
