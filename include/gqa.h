@@ -81,7 +81,11 @@ typedef enum gqa_dtype { GQA_BF16 = 0, GQA_FP32 = 1, GQA_FP16 = 2 } gqa_dtype;
  * several slices is merged with a log-sum-exp combine in a second launch on
  * the same stream. The fp32 partial rows live in a library-owned workspace,
  * one per (device, stream), allocated with stream-ordered allocation on first
- * use, grown when needed, and kept until the process ends.
+ * use, grown when needed, and kept until the process ends. Results are
+ * bit-identical from call to call. Graph capture: make one call of the same
+ * (or a larger) shape on the capture stream before capturing, so that the
+ * captured calls find the workspace and allocate nothing; the captured graph
+ * then reads seqlens and the tensors at replay time.
  * Requires 1 <= G, G divides H, Tmax >= 0, d_h in {64, 128}.
  */
 gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens,
