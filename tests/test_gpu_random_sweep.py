@@ -181,3 +181,28 @@ def test_random_decode_large_scores(case):
                          split_tokens=split)
     torch.cuda.synchronize()
     assert_parity(out, ref, dtype, f"large-score decode #{i}")
+
+
+@pytest.mark.parametrize("B", [64, 65, 128, 129, 300])
+@pytest.mark.parametrize("append,window,split", [(False, 0, 0), (True, 0, 0), (True, 37, 0), (False, 0, 64)])
+def test_decode_many_sequences(B, append, window, split):
+    """More than 64 sequences: the partition, the walk over the sequences and
+    the merge go through the lengths 64 at a time."""
+    rng = random.Random(B * 7 + window + split)
+    Tmax = 200
+    seqlens = [rng.choice([0, 1, 31, 32, 33, Tmax, rng.randint(1, Tmax)]) for _ in range(B)]
+    say(f"decode with {B} sequences append={append} window={window} split={split}")
+    w = I.DecodeWorkload("many", B, 8, 2, 128, Tmax, torch.bfloat16)
+    x = I.decode_inputs(w, seed=B, device=DEV, seqlens=seqlens)
+    kn = I.random_tensor((B, 2, 128), seed=B + 1, dtype=torch.bfloat16, device=DEV) if append else None
+    vn = I.random_tensor((B, 2, 128), seed=B + 2, dtype=torch.bfloat16, device=DEV) if append else None
+    ref, k_ref, v_ref = O.decode_step(to_host(x["q"]), to_host(x["k_cache"]), to_host(x["v_cache"]),
+                                      to_host(x["seqlens"]), w.scale,
+                                      k_new=to_host(kn) if append else None, v_new=to_host(vn) if append else None,
+                                      window=window)
+    torch.cuda.synchronize()
+    out = gq.decode_step(x["q"], x["k_cache"], x["v_cache"], x["seqlens"], scale=w.scale, k_new=kn, v_new=vn,
+                         window=window, split_tokens=split)
+    torch.cuda.synchronize()
+    assert_parity(out, ref, torch.bfloat16, f"{B} sequences")
+    assert np.array_equal(_bits(x["k_cache"]), k_ref) and np.array_equal(_bits(x["v_cache"]), v_ref)
