@@ -106,16 +106,18 @@ __device__ __forceinline__ Span seq_span(int32_t s, int Tmax, int append, int wi
 // Flat-position partition shared by the decode and merge kernels (both must
 // compute identical values): total positions and the piece length P. The
 // host guarantees B * Tmax < 2^31, so position counts fit in 32 bits.
+// `n_first` is this lane's span length among the first 64 sequences (0 past
+// B); the caller has read those lengths already and keeps them for its walk.
 struct Partition {
     int64_t total;
     int64_t P;
 };
 
-__device__ __forceinline__ Partition make_partition(const int32_t *seqlens, int B, int Tmax, int append, int window,
-                                                    int nwg, int fixed_P, int lane)
+__device__ __forceinline__ Partition make_partition(int n_first, const int32_t *seqlens, int B, int Tmax, int append,
+                                                    int window, int nwg, int fixed_P, int lane)
 {
-    int part = 0;
-    for (int i = lane; i < B; i += 64)
+    int part = n_first;
+    for (int i = lane + 64; i < B; i += 64)
         part += seq_span(seqlens[i], Tmax, append, window).n;
     const int64_t tot = wave_total(part);
     int64_t P;
@@ -379,7 +381,11 @@ decode_split_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const 
     const int h0 = g * r + ht * C::HEADS;
     const int nheads = min(C::HEADS, r - ht * C::HEADS);
 
-    const Partition pt = make_partition(seqlens, B, Tmax, APPEND, window, nwg, fixed_P, lane);
+    // The first 64 lengths are read once, for the partition and the walk.
+    Span sp0 = {0, 0, false};
+    if (lane < B)
+        sp0 = seq_span(seqlens[lane], Tmax, APPEND, window);
+    const Partition pt = make_partition(sp0.n, seqlens, B, Tmax, APPEND, window, nwg, fixed_P, lane);
     const int64_t lo = (int64_t)k * pt.P;
     if (lo >= pt.total)
         return;
@@ -388,9 +394,12 @@ decode_split_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const 
     // Walk the sequences overlapping [lo, hi), 64 lengths at a time.
     int64_t pre = 0;
     for (int b0 = 0; b0 < B; b0 += 64) {
-        Span sp = {0, 0, false};
-        if (b0 + lane < B)
-            sp = seq_span(seqlens[b0 + lane], Tmax, APPEND, window);
+        Span sp = sp0;
+        if (b0 > 0) {
+            sp = {0, 0, false};
+            if (b0 + lane < B)
+                sp = seq_span(seqlens[b0 + lane], Tmax, APPEND, window);
+        }
         const int Lc = sp.n;
         const int incl = wave_incl_scan(Lc);
         const int64_t chunk_total = __builtin_amdgcn_readlane(incl, 63);
@@ -452,12 +461,14 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
         return;
 
     // partition and this sequence's first flat position (each wave on its own)
-    int tot_part = 0, pre_part = 0;
+    int tot_part = 0, pre_part = 0, L_first = 0;
     for (int i = lane; i < B; i += 64) {
         const int Li = seq_span(seqlens[i], Tmax, append, window).n;
         tot_part += Li;
         if (i < b)
             pre_part += Li;
+        if (i == lane)
+            L_first = Li;
     }
     const int64_t tot = wave_total(tot_part);
     const int64_t pre_b = wave_total(pre_part);
@@ -475,7 +486,7 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
     const int sl = lane / NQ, qd = lane % NQ;
     const int d0 = dc * DCH + qd * 4;
     __bf16 *dst = out + ((int64_t)b * H + h) * D + d0;
-    const int L = seq_span(seqlens[b], Tmax, append, window).n;
+    const int L = b < 64 ? __builtin_amdgcn_readlane(L_first, b) : seq_span(seqlens[b], Tmax, append, window).n;
     if (L == 0) {
         if (sl == 0)
             *reinterpret_cast<u32x2_t *>(dst) = (u32x2_t){0, 0};
