@@ -215,6 +215,9 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
     // of this tile run. The K/V pointers are deliberately not __restrict__
     // (with it the loads count as invariant and get moved across the fences
     // below), and the scheduling barriers keep each request at its place.
+    // (Two tiles in flight per wave measured slower, also for the waves of
+    // 32-head tiles that have a SIMD to themselves.)
+    const int stride = WPG * kTile;
     int t0 = ta + sub * kTile;
     const bool any_tile = t0 < tb;  // wave-uniform
     u32x4_t kbuf[2][C::KS], vbuf[C::VLOADS];
@@ -222,8 +225,9 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
         load_k(t0, kbuf);
         load_v(t0, vbuf);
     }
-    while (any_tile) {
-        const int tn = t0 + WPG * kTile;
+    auto tile = [&](u32x4_t (&kbf)[2][C::KS], u32x4_t (&vbf)[C::VLOADS], const int tc)
+                    __attribute__((always_inline)) {
+        const int tn = tc + stride;  // the tile these buffers take next
 
         // S^T = K q^T for two 16-token row tiles.
         f32x4_t st[2][NT];
@@ -234,24 +238,24 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
                 f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < C::KS; ++s)
-                    c = mfma16x16x32<T>(__builtin_bit_cast(bf16x8_t, kbuf[mt][s]), qf[nt][s], c);
+                    c = mfma16x16x32<T>(__builtin_bit_cast(bf16x8_t, kbf[mt][s]), qf[nt][s], c);
                 st[mt][nt] = c;
             }
         if constexpr (APPEND) {
             // the lanes holding the appended token's key row store it
-            if (store_new && t_new >= t0 && t_new < t0 + kTile) {
+            if (store_new && t_new >= tc && t_new < tc + kTile) {
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
-                    if (t0 + mt * 16 + col == t_new) {
+                    if (tc + mt * 16 + col == t_new) {
 #pragma unroll
                         for (int s = 0; s < C::KS; ++s)
-                            *reinterpret_cast<u32x4_t *>(kbase + t_new * tok_stride + (s * 4 + kb) * 8) = kbuf[mt][s];
+                            *reinterpret_cast<u32x4_t *>(kbase + t_new * tok_stride + (s * 4 + kb) * 8) = kbf[mt][s];
                     }
             }
         }
         compiler_fence();
         __builtin_amdgcn_sched_barrier(0);
-        load_k(tn, kbuf);  // clamped prefetch, also past the end
+        load_k(tn, kbf);  // clamped prefetch, also past the end
         compiler_fence();
         __builtin_amdgcn_sched_barrier(0);
 
@@ -262,19 +266,19 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
             const int tl = i * C::VROWS + lane / C::CH;
             const u32x4_t zero = {0, 0, 0, 0};
             *reinterpret_cast<u32x4_t *>(vl + tl * C::LDS_STRIDE + (lane % C::CH) * 8) =
-                (t0 + tl < tb) ? vbuf[i] : zero;
+                (tc + tl < tb) ? vbf[i] : zero;
             if constexpr (APPEND) {
-                if (store_new && t0 + tl == t_new)
-                    *reinterpret_cast<u32x4_t *>(vbase + t_new * tok_stride + (lane % C::CH) * 8) = vbuf[i];
+                if (store_new && tc + tl == t_new)
+                    *reinterpret_cast<u32x4_t *>(vbase + t_new * tok_stride + (lane % C::CH) * 8) = vbf[i];
             }
         }
         compiler_fence();
         __builtin_amdgcn_sched_barrier(0);
-        load_v(tn, vbuf);
+        load_v(tn, vbf);
         compiler_fence();
         __builtin_amdgcn_sched_barrier(0);
 
-        // Online softmax (base 2). Lane holds tokens t0 + 16*mt + 4*kb + i of head column col.
+        // Online softmax (base 2). Lane holds tokens tc + 16*mt + 4*kb + i of head column col.
         bf16x8_t pf[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -283,7 +287,7 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int t = t0 + mt * 16 + kb * 4 + i;
+                    const int t = tc + mt * 16 + kb * 4 + i;
                     const float x = (t < tb) ? st[mt][nt][i] * scale_log2 : -INFINITY;
                     st[mt][nt][i] = x;
                     mx = fmaxf(mx, x);
@@ -324,9 +328,14 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
                 acc[nt][dt] = mfma16x16x32<T>(vf, pf[nt], acc[nt][dt]);
         }
 
-        if (tn >= tb)
-            break;
-        t0 = tn;
+    };
+    if (any_tile) {
+        for (;;) {
+            tile(kbuf, vbuf, t0);
+            if (t0 + stride >= tb)
+                break;
+            t0 += stride;
+        }
     }
 
     // Finish: the four lanes of one head column hold disjoint token subsets'
