@@ -241,18 +241,6 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
                     c = mfma16x16x32<T>(__builtin_bit_cast(bf16x8_t, kbf[mt][s]), qf[nt][s], c);
                 st[mt][nt] = c;
             }
-        if constexpr (APPEND) {
-            // the lanes holding the appended token's key row store it
-            if (store_new && t_new >= tc && t_new < tc + kTile) {
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-                    if (tc + mt * 16 + col == t_new) {
-#pragma unroll
-                        for (int s = 0; s < C::KS; ++s)
-                            *reinterpret_cast<u32x4_t *>(kbase + t_new * tok_stride + (s * 4 + kb) * 8) = kbf[mt][s];
-                    }
-            }
-        }
         compiler_fence();
         __builtin_amdgcn_sched_barrier(0);
         load_k(tn, kbf);  // clamped prefetch, also past the end
@@ -267,10 +255,6 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
             const u32x4_t zero = {0, 0, 0, 0};
             *reinterpret_cast<u32x4_t *>(vl + tl * C::LDS_STRIDE + (lane % C::CH) * 8) =
                 (tc + tl < tb) ? vbf[i] : zero;
-            if constexpr (APPEND) {
-                if (store_new && tc + tl == t_new)
-                    *reinterpret_cast<u32x4_t *>(vbase + t_new * tok_stride + (lane % C::CH) * 8) = vbf[i];
-            }
         }
         compiler_fence();
         __builtin_amdgcn_sched_barrier(0);
@@ -335,6 +319,21 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
             if (t0 + stride >= tb)
                 break;
             t0 += stride;
+        }
+    }
+
+    // The appended token's rows go from k_new / v_new to the cache, written
+    // by one wave of the group after the loop: no wave reads that cache row
+    // in this call (its tile loads take the row from k_new / v_new). Stores
+    // inside the loop would be conditional, and a store that may or may not
+    // have been issued leaves the compiler unsure how many memory operations
+    // are outstanding, so it would wait for all of them at every tile.
+    if constexpr (APPEND) {
+        if (store_new && sub == 0 && t_new >= 0 && lane < C::CH) {
+            const u32x4_t kx = load16(knew_row + lane * 8);
+            const u32x4_t vx = load16(vnew_row + lane * 8);
+            *reinterpret_cast<u32x4_t *>(kbase + t_new * tok_stride + lane * 8) = kx;
+            *reinterpret_cast<u32x4_t *>(vbase + t_new * tok_stride + lane * 8) = vx;
         }
     }
 
