@@ -38,7 +38,8 @@
 //    reads them again (one head tile per group): the streaming cache policy
 //    raised the achieved bandwidth by 6-7%.
 //  * Online softmax in base 2 (the fp32 scores are multiplied by
-//    scale*log2(e)); row maxima use two cross-lane exchanges per tile.
+//    scale*log2(e)); row maxima use two VALU lane swaps per tile (not LDS
+//    permutes, which would wait behind the tile's V^T reads).
 //  * A sequence that lies wholly inside one wave's piece is written to `out`
 //    directly. Otherwise each piece writes a normalised fp32 partial row and
 //    its base-2 log-sum-exp, and a second, small kernel merges the partials of
@@ -276,8 +277,8 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
                     st[mt][nt][i] = x;
                     mx = fmaxf(mx, x);
                 }
-            mx = wave_max_xor(mx, 16);
-            mx = wave_max_xor(mx, 32);
+            mx = xor_fmax<16>(mx);
+            mx = xor_fmax<32>(mx);
             const float m_new = fmaxf(m_run[nt], mx);
             const float alpha = fast_exp2(m_run[nt] - m_new);
             m_run[nt] = m_new;
@@ -341,8 +342,8 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
     // weight sums; the accumulator lane holds O^T[dt*16 + 4*kb + i][head].
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        l_run[nt] += __shfl_xor(l_run[nt], 16, 64);
-        l_run[nt] += __shfl_xor(l_run[nt], 32, 64);
+        l_run[nt] = xor_add<16>(l_run[nt]);
+        l_run[nt] = xor_add<32>(l_run[nt]);
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {

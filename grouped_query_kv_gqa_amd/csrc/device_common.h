@@ -122,6 +122,50 @@ __device__ __forceinline__ float wave_max_xor(float x, int mask)
     return fmaxf(x, __shfl_xor(x, mask, 64));
 }
 
+// x of this lane and of lane l ^ MASK (MASK = 16 or 32), exchanged by the
+// VALU lane swaps (v_permlane16_swap / v_permlane32_swap with both operands
+// x): `a`, `b` are the two values, in an order that differs between the two
+// lanes of a pair, so their maximum or sum is the same in both lanes. Unlike
+// __shfl_xor (ds_bpermute) the swap does not go through the LDS queue and
+// never waits behind outstanding LDS reads. Lane layout checked on gfx950.
+// The two results are copied to scalars before the bit casts: clang's
+// __builtin_bit_cast of a vector element expression reads the vector's first
+// element whatever the index.
+template <int MASK>
+__device__ __forceinline__ void xor_pair(float x, float &a, float &b)
+{
+    static_assert(MASK == 16 || MASK == 32, "lane swaps exchange rows of 16 or halves of 32");
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    uint32_t s0, s1;
+    if constexpr (MASK == 32) {
+        const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        s0 = s[0];
+        s1 = s[1];
+    } else {
+        const auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        s0 = s[0];
+        s1 = s[1];
+    }
+    a = __builtin_bit_cast(float, s0);
+    b = __builtin_bit_cast(float, s1);
+}
+
+template <int MASK>
+__device__ __forceinline__ float xor_fmax(float x)
+{
+    float a, b;
+    xor_pair<MASK>(x, a, b);
+    return fmaxf(a, b);
+}
+
+template <int MASK>
+__device__ __forceinline__ float xor_add(float x)
+{
+    float a, b;
+    xor_pair<MASK>(x, a, b);
+    return a + b;
+}
+
 __device__ __forceinline__ float wave_sum(float x)
 {
 #pragma unroll

@@ -386,7 +386,11 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     float delta = 0.f;
     auto max_finish = [&](float mx0, float mx1) {
         float mx = __builtin_elementwise_maximum(mx0, mx1);
-        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32, 64));
+        {
+            float a, b;
+            xor_pair<32>(mx, a, b);  // VALU lane swap: does not queue behind LDS reads
+            mx = __builtin_elementwise_maximum(a, b);
+        }
         mx = fmaf(mx, scale_log2, -m_run);  // scaled, relative to m_run (-inf stays -inf)
         const bool first = WIN && !m_set && mx != -INFINITY;  // O and l are still zero
         move = mx > kLazy || first;
@@ -592,7 +596,11 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         for (int v = 0; v < 16; v += 2)
             max_part(st[0], v, mx0, mx1);
         float mx = __builtin_elementwise_maximum(mx0, mx1);
-        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32, 64));
+        {
+            float a, b;
+            xor_pair<32>(mx, a, b);  // VALU lane swap: does not queue behind LDS reads
+            mx = __builtin_elementwise_maximum(a, b);
+        }
         m_set = mx != -INFINITY;
         m_run = m_set ? mx * scale_log2 : 0.f;
     }
@@ -622,7 +630,7 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         tail(j);
 
     // Epilogue: lane holds O^T[dt*32 + 8*m0 + 4*h + m1][row]; 4 consecutive d per (dt, m0).
-    const float lsum = l_run + __shfl_xor(l_run, 32, 64);
+    const float lsum = xor_add<32>(l_run);
     if (!row_ok)
         return;
     const float inv = 1.f / lsum;
