@@ -457,8 +457,7 @@ decode_split_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const 
 template <typename T, int D, int NQ>
 __global__ void __launch_bounds__(256)
 decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax, int append, int window, int nwg,
-                    int fixed_P, int wpg, const float *__restrict__ part, const float *__restrict__ lse,
-                    __bf16 *__restrict__ out)
+                    int fixed_P, int wpg, const float *part, const float *lse, __bf16 *__restrict__ out)
 {
     constexpr int DCH = 4 * NQ;      // d values per item
     constexpr int NDC = D / DCH;     // items per row
@@ -509,6 +508,7 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
 
     float m = -INFINITY, den = 0.f;
     f32x4_t num = {0.f, 0.f, 0.f, 0.f};
+    const int lw = __builtin_ctz(wpg);  // wpg = waves per group, a power of two
     constexpr int U = 4;  // slots per lane per round, loads issued together
     for (int j0 = sl; j0 < nslots; j0 += NS * U) {
         float x[U];
@@ -516,11 +516,17 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int j = min(j0 + NS * u, nslots - 1);
-            const int64_t piece = k_first + j / wpg + b;
-            const int64_t idx = (piece * H + h) * wpg + j % wpg;
+            const int64_t piece = k_first + (j >> lw) + b;
+            const int64_t idx = (piece * H + h) * wpg + (j & (wpg - 1));
             x[u] = lse[idx];
             pv[u] = *reinterpret_cast<const f32x4_t *>(part + idx * D + d0);
         }
+        // All loads of the round are issued before any is used (the compiler
+        // otherwise sinks the last one into the branch that uses it, behind a
+        // wait for the first). The partial pointers are not __restrict__ for
+        // the same reason: with it the loads may move across this fence.
+        compiler_fence();
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (j0 + NS * u >= nslots || x[u] == -INFINITY)
