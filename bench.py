@@ -98,7 +98,8 @@ def timed_launches(fn, steps, warmup, stream, every=1):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     region_ms = e0.elapsed_time(e1) / steps
-    sampled = [i for i in range(steps) if i % every == every // 2]
+    # every `every`-th launch, and at least one (short runs, e.g. under a profiler)
+    sampled = [i for i in range(steps) if i % every == every // 2] or [0]
     ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in sampled}
     for i in range(steps):
         e = ev.get(i)
