@@ -38,6 +38,10 @@ BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published (256 CU x 2.
 METRIC = "GQA decode HBM GB/s (% of peak) + causal prefill TFLOP/s (% MFMA peak), bf16"
 DECODE_WORKLOAD = "decode_llama3_8b"
 PREFILL_WORKLOAD = "prefill_llama3_8b_causal"
+TRAFFIC_PROFILES = {  # rocprofv3 FETCH_SIZE / WRITE_SIZE summaries, one per timed kernel and workload
+    "decode": "decode_llama3_8b_hbm_counters.md",
+    "prefill": "prefill_b4_t8192_hbm_counters.md",
+}
 KERNEL_SOURCES = {
     "decode": ["grouped_query_kv_gqa_amd/csrc/decode.hip", "grouped_query_kv_gqa_amd/csrc/device_common.h"],
     "prefill": ["grouped_query_kv_gqa_amd/csrc/prefill.hip", "grouped_query_kv_gqa_amd/csrc/device_common.h"],
@@ -55,7 +59,7 @@ def source_hash(kind: str) -> str:
 def measured_traffic(kind: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when it is missing or was taken on other kernel source."""
-    path = os.path.join(ROOT, "profiles", f"{kind}_counters.md")
+    path = os.path.join(ROOT, "profiles", TRAFFIC_PROFILES[kind])
     if not os.path.exists(path):
         return None
     m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
