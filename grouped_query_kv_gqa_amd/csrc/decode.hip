@@ -146,9 +146,11 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
                                              int h0, int nheads, int t_off, int ta, int tb, int t_new,
                                              const __bf16 *knew_row, const __bf16 *vnew_row, bool store_new,
                                              bool whole, int H, int G, int Tmax, int sub, float scale_log2,
-                                             __bf16 *vl, __bf16 *__restrict__ out, float *__restrict__ part_row,
-                                             float *__restrict__ lse_row, int64_t part_stride, int lane)
+                                             __bf16 *vl_all, __bf16 *__restrict__ out, float *__restrict__ part_row,
+                                             float *__restrict__ lse_row, int lane)
 {
+    const int wave = threadIdx.x >> 6;
+    __bf16 *vl = vl_all + wave * kTile * TileCfg<D, NT>::LDS_STRIDE;  // this wave's V tile
     using C = TileCfg<D, NT>;
     const int col = lane & 15, kb = lane >> 4;
     const int64_t row0 = (int64_t)b * H + h0;
@@ -345,28 +347,81 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
         l_run[nt] = xor_add<16>(l_run[nt]);
         l_run[nt] = xor_add<32>(l_run[nt]);
     }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    // Output of one head tile: the finished rows when the piece holds the
+    // whole sequence, else a normalised fp32 partial row per head and its
+    // base-2 log-sum-exp. Lane (col, kb) holds d = dt*16 + 4*kb + i.
+    auto emit = [&](int nt, int dt, const f32x4_t &o, float inv) {
         const int hh = nt * 16 + col;
         if (hh >= nheads)
-            continue;
-        const float inv = l_run[nt] > 0.f ? 1.f / l_run[nt] : 0.f;
+            return;
         if (whole) {
-            __bf16 *dst = out + (row0 + hh) * D + kb * 4;
-#pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt) {
-                const f32x4_t o = acc[nt][dt] * inv;
-                u32x2_t u = {pack2<T>(o[0], o[1]), pack2<T>(o[2], o[3])};
-                *reinterpret_cast<u32x2_t *>(dst + dt * 16) = u;
-            }
+            const f32x4_t x = o * inv;
+            u32x2_t u = {pack2<T>(x[0], x[1]), pack2<T>(x[2], x[3])};
+            *reinterpret_cast<u32x2_t *>(out + (row0 + hh) * D + kb * 4 + dt * 16) = u;
         } else {
-            float *dst = part_row + hh * part_stride * D + kb * 4;
+            *reinterpret_cast<f32x4_t *>(part_row + hh * D + kb * 4 + dt * 16) = o * inv;
+        }
+    };
+    if constexpr (WPG == 1) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const float inv = l_run[nt] > 0.f ? 1.f / l_run[nt] : 0.f;
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt)
-                *reinterpret_cast<f32x4_t *>(dst + dt * 16) = acc[nt][dt] * inv;
-            if (kb == 0)
-                lse_row[hh * part_stride] = l_run[nt] > 0.f ? m_run[nt] + fast_log2(l_run[nt]) : -INFINITY;
+                emit(nt, dt, acc[nt][dt], inv);
+            if (!whole && kb == 0 && nt * 16 + col < nheads)
+                lse_row[nt * 16 + col] = l_run[nt] > 0.f ? m_run[nt] + fast_log2(l_run[nt]) : -INFINITY;
         }
+    } else {
+        // The WPG waves of this group each hold the softmax state of every
+        // WPG-th tile. They are combined here, through the V tiles' LDS
+        // (free once every wave has left its loop), into one row per head:
+        // each wave publishes its maxima, sums and unnormalised accumulators,
+        // then combines every WPG-th d tile of all of them. One partial row
+        // per head (or the finished output) leaves the workgroup, not WPG.
+        constexpr int REG = kTile * C::LDS_STRIDE / 2;  // floats in one wave's V tile
+        constexpr int ML = C::DT * 256;                 // offset of the maxima and sums
+        static_assert(ML + 32 <= REG, "a wave's state fits in its V tile");
+        float *lds = reinterpret_cast<float *>(vl_all);
+        float *mine = lds + wave * REG;
+        const float *grp = lds + (wave - sub) * REG;  // the group's first wave
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            __syncthreads();  // every wave is done with its V tile (or the previous head tile)
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt)
+                *reinterpret_cast<f32x4_t *>(mine + dt * 256 + lane * 4) = acc[nt][dt];
+            if (kb == 0) {
+                mine[ML + col] = m_run[nt];
+                mine[ML + 16 + col] = l_run[nt];
+            }
+            __syncthreads();
+            float M = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < WPG; ++j)
+                M = fmaxf(M, grp[j * REG + ML + col]);
+            float wj[WPG], L = 0.f;
+#pragma unroll
+            for (int j = 0; j < WPG; ++j) {
+                const float mj = grp[j * REG + ML + col];
+                wj[j] = mj == -INFINITY ? 0.f : fast_exp2(mj - M);
+                L += wj[j] * grp[j * REG + ML + 16 + col];
+            }
+            const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) {
+                if (dt % WPG != sub)
+                    continue;
+                f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < WPG; ++j)
+                    o += wj[j] * *reinterpret_cast<const f32x4_t *>(grp + j * REG + dt * 256 + lane * 4);
+                emit(nt, dt, o, inv);
+            }
+            if (!whole && sub == 0 && kb == 0 && nt * 16 + col < nheads)
+                lse_row[nt * 16 + col] = L > 0.f ? M + fast_log2(L) : -INFINITY;
+        }
+        __syncthreads();  // the next piece's loop refills the V tiles
     }
 }
 
@@ -427,10 +482,10 @@ decode_split_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const 
             const int b = b0 + i;
             const int ta = (int)max<int64_t>(lo - pre_b, 0);
             const int tb = (int)min<int64_t>(hi - pre_b, L);
-            const bool whole = (WPG == 1) && ta == 0 && tb == L;
+            const bool whole = ta == 0 && tb == L;
             const int64_t piece = (int64_t)k + b;
-            // partial layout [piece][head][sub][d], log-sum-exp [piece][head][sub]
-            const int64_t slot = (piece * H + h0) * WPG + sub;
+            // partial layout [piece][head][d], log-sum-exp [piece][head]
+            const int64_t slot = piece * H + h0;
             const int lo_b = __builtin_amdgcn_readlane(sp.lo, i);
             // The appended token is the span's last position, so only the piece
             // that ends there holds it. An earlier piece's last tile can reach
@@ -441,7 +496,7 @@ decode_split_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const 
             const int64_t new_off = ((int64_t)b * G + g) * D;
             decode_piece<T, D, NT, WPG, APPEND>(q, kc, vc, b, g, h0, nheads, lo_b, ta, tb, t_new, knew + new_off,
                                              vnew + new_off, ht == 0, whole, H, G, Tmax, sub, scale_log2,
-                                             &vlds[wave][0], out, part + slot * D, lse + slot, WPG, lane);
+                                             &vlds[0][0], out, part + slot * D, lse + slot, lane);
         }
         pre += chunk_total;
     }
@@ -457,7 +512,7 @@ decode_split_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const 
 template <typename T, int D, int NQ>
 __global__ void __launch_bounds__(256)
 decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax, int append, int window, int nwg,
-                    int fixed_P, int wpg, const float *part, const float *lse, __bf16 *__restrict__ out)
+                    int fixed_P, const float *part, const float *lse, __bf16 *__restrict__ out)
 {
     constexpr int DCH = 4 * NQ;      // d values per item
     constexpr int NDC = D / DCH;     // items per row
@@ -502,13 +557,12 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
     }
     const int64_t k_first = pre_b / P;
     const int64_t k_last = (pre_b + L - 1) / P;
-    if (k_first == k_last && wpg == 1)
+    if (k_first == k_last)
         return;  // written whole by the decode kernel
-    const int nslots = (int)(k_last - k_first + 1) * wpg;
+    const int nslots = (int)(k_last - k_first + 1);
 
     float m = -INFINITY, den = 0.f;
     f32x4_t num = {0.f, 0.f, 0.f, 0.f};
-    const int lw = __builtin_ctz(wpg);  // wpg = waves per group, a power of two
     constexpr int U = 4;  // slots per lane per round, loads issued together
     for (int j0 = sl; j0 < nslots; j0 += NS * U) {
         float x[U];
@@ -516,8 +570,7 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int j = min(j0 + NS * u, nslots - 1);
-            const int64_t piece = k_first + (j >> lw) + b;
-            const int64_t idx = (piece * H + h) * wpg + (j & (wpg - 1));
+            const int64_t idx = (k_first + j + b) * H + h;  // slot of piece k_first + j
             x[u] = lse[idx];
             pv[u] = *reinterpret_cast<const f32x4_t *>(part + idx * D + d0);
         }
@@ -565,26 +618,26 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
 }
 
 template <typename T, int D, int NQ>
-hipError_t launch_merge(const DecodePlan &p, const DecodeArgs &a, int wpg)
+hipError_t launch_merge(const DecodePlan &p, const DecodeArgs &a)
 {
     constexpr int NDC = D / (4 * NQ);
     dim3 grid((unsigned)((a.H * NDC + 3) / 4), (unsigned)a.B);
     decode_merge_kernel<T, D, NQ><<<grid, 256, 0, a.stream>>>(a.seqlens, a.B, a.H, a.Tmax, a.knew != nullptr,
-                                                          a.window, p.nwg, p.fixed_P, wpg, a.part, a.lse,
+                                                          a.window, p.nwg, p.fixed_P, a.part, a.lse,
                                                           static_cast<__bf16 *>(a.out));
     return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t launch_merge_d(const DecodePlan &p, const DecodeArgs &a, int wpg)
+hipError_t launch_merge_d(const DecodePlan &p, const DecodeArgs &a)
 {
     switch (p.merge_nq) {
-    case 1: return launch_merge<T, D, 1>(p, a, wpg);
-    case 2: return launch_merge<T, D, 2>(p, a, wpg);
-    case 4: return launch_merge<T, D, 4>(p, a, wpg);
-    case 8: return launch_merge<T, D, 8>(p, a, wpg);
-    case 16: return launch_merge<T, D, 16>(p, a, wpg);
-    default: return launch_merge<T, D, (D >= 128 ? 32 : 16)>(p, a, wpg);
+    case 1: return launch_merge<T, D, 1>(p, a);
+    case 2: return launch_merge<T, D, 2>(p, a);
+    case 4: return launch_merge<T, D, 4>(p, a);
+    case 8: return launch_merge<T, D, 8>(p, a);
+    case 16: return launch_merge<T, D, 16>(p, a);
+    default: return launch_merge<T, D, (D >= 128 ? 32 : 16)>(p, a);
     }
 }
 
@@ -670,7 +723,7 @@ hipError_t launch_split(const DecodePlan &p, const DecodeArgs &a)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    return launch_merge_d<T, D>(p, a, WAVES / GB);
+    return launch_merge_d<T, D>(p, a);
 }
 
 // Dispatch over the compiled variants: (d_h, head tiles NT, waves, groups per workgroup GB).

@@ -184,7 +184,7 @@ gqa_status plan_decode(int B, int H, int G, int d_h, int Tmax, gqa_dtype dtype, 
     // Merge layout: enough slot lanes that each takes at most 4 pieces of a
     // full-length row, the rest of the 64 lanes spread over d.
     {
-        const int64_t exp_slots = (ceil_div(Tmax > 0 ? Tmax : 1, p.full_P) + 1) * (p.waves / p.gb);
+        const int64_t exp_slots = ceil_div(Tmax > 0 ? Tmax : 1, p.full_P) + 1;
         int64_t ns = 1;
         while (ns < 64 && ns * 4 < exp_slots)
             ns *= 2;
@@ -193,7 +193,9 @@ gqa_status plan_decode(int B, int H, int G, int d_h, int Tmax, gqa_dtype dtype, 
             ns = min_ns;
         p.merge_nq = (int)(64 / ns);
     }
-    const int64_t slots = (nwg + B) * (int64_t)H * (p.waves / p.gb);
+    // One partial row per (piece, head): the waves that share a group combine
+    // their states inside the workgroup before anything is written.
+    const int64_t slots = (nwg + B) * (int64_t)H;
     p.part_offset = 0;
     p.lse_offset = round_up(slots * d_h * 4, 256);
     p.workspace_bytes = round_up(p.lse_offset + slots * 4, 256);

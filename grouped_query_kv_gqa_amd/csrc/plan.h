@@ -23,8 +23,8 @@ struct DecodePlan {
     int fixed_P = 0;     // piece length when set by the caller, else 0 (balanced on the device)
     int full_P = 32;     // piece length when every sequence has Tmax positions
     int merge_nq = 8;    // merge kernel: d-quads per wave (64/merge_nq lanes share a quad)
-    int64_t part_offset = 0;      // fp32 partial rows [nwg + B][H][waves/gb][d_h]
-    int64_t lse_offset = 0;       // fp32 base-2 log-sum-exp [nwg + B][H][waves/gb]
+    int64_t part_offset = 0;      // fp32 partial rows [nwg + B][H][d_h]
+    int64_t lse_offset = 0;       // fp32 base-2 log-sum-exp [nwg + B][H]
     int64_t workspace_bytes = 0;  // 0 for the fp32 path
 };
 

@@ -116,8 +116,8 @@ int main() {
       if (B == 0) continue;
       assert(p.nwg >= 1 && p.full_P >= 32 && p.full_P % 32 == 0);
       assert((int64_t)p.full_P * p.nwg >= (int64_t)B * T);
-      assert(p.workspace_bytes >= p.lse_offset + ((int64_t)p.nwg + B) * H * (p.waves / p.gb) * 4);
-      assert(p.lse_offset >= ((int64_t)p.nwg + B) * H * (p.waves / p.gb) * 128 * 4);
+      assert(p.workspace_bytes >= p.lse_offset + ((int64_t)p.nwg + B) * H * 4);
+      assert(p.lse_offset >= ((int64_t)p.nwg + B) * H * 128 * 4);
     }
   }
   assert(gqa::plan_decode(1, 6, 4, 128, 10, GQA_BF16, 0, 256, 0, &p, &e) == GQA_ERR_INVALID_ARG);
