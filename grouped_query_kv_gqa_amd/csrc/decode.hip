@@ -40,10 +40,14 @@
 //  * Online softmax in base 2 (the fp32 scores are multiplied by
 //    scale*log2(e)); row maxima use two VALU lane swaps per tile (not LDS
 //    permutes, which would wait behind the tile's V^T reads).
-//  * A sequence that lies wholly inside one wave's piece is written to `out`
-//    directly. Otherwise each piece writes a normalised fp32 partial row and
-//    its base-2 log-sum-exp, and a second, small kernel merges the partials of
-//    every row (the kernel boundary orders the two; no atomics are used).
+//  * Waves that share a group (WAVES/GB > 1) combine their softmax states in
+//    LDS at the end of each piece, so a piece always leaves the workgroup as
+//    one row per head.
+//  * A sequence that lies wholly inside one workgroup's piece is written to
+//    `out` directly. Otherwise each piece writes a normalised fp32 partial
+//    row and its base-2 log-sum-exp, and a second, small kernel merges the
+//    partials of every row (the kernel boundary orders the two; no atomics
+//    are used).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -135,8 +139,11 @@ __device__ __forceinline__ Partition make_partition(int n_first, const int32_t *
 
 // One wave's work on one piece: positions [ta, tb) of sequence b for the
 // heads [h0, h0 + nheads) of group g. The wave takes tiles ta + sub*32,
-// ta + (sub + WPG)*32, ... Writes the finished rows to `out` when `whole`,
-// else a normalised partial row per head and its base-2 log-sum-exp.
+// ta + (sub + WPG)*32, ...; with WPG > 1 the group's waves then combine
+// their states (every wave of the workgroup must call this for the same
+// pieces: the combine has workgroup barriers). Writes the finished rows to
+// `out` when `whole`, else a normalised partial row per head and its base-2
+// log-sum-exp. `vl_all` is the workgroup's V-tile LDS, one tile per wave.
 //
 // APPEND: position t_new (relative to the span, or -1) is the appended token:
 // its rows come from knew_row/vnew_row (this group's slice of k_new, v_new)
