@@ -49,10 +49,15 @@ KERNEL_SOURCES = {
 
 
 def source_hash(kind: str) -> str:
+    """Hash of the kernel sources without comments and blank lines, so that a
+    comment edit does not mark the committed counters as taken on other code."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(line.rstrip() for line in text.splitlines() if line.strip()).encode())
     return h.hexdigest()[:16]
 
 
