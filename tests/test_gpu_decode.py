@@ -221,3 +221,31 @@ def test_decode_llama3_8b_fp16_full():
     ref = O.decode(to_host(x["q"]), to_host(x["k_cache"]), to_host(x["v_cache"]), to_host(x["seqlens"]), w.scale)
     ma, rl = assert_parity(out, ref, w.dtype, w.name)
     print(f"{w.name}: max-abs {ma:.3e} rel-L2 {rl:.3e}")
+
+
+@pytest.mark.parametrize("H,G", [(8, 2), (16, 4), (24, 3), (64, 1), (48, 1), (96, 2)])
+def test_decode_shared_group_deterministic(H, G):
+    """Layouts where several waves share a group (they combine their softmax
+    states inside the workgroup): repeated calls give the same bits, and the
+    result matches the oracle, with and without an append."""
+    say(f"decode deterministic combine H={H} G={G}")
+    B, D, Tmax = 6, 128, 1500
+    w = I.DecodeWorkload("det", B, H, G, D, Tmax, torch.bfloat16)
+    x = I.decode_inputs(w, seed=H * 10 + G, device=DEV, seqlens=[1500, 1, 700, 0, 1499, 333])
+    ref = O.decode(to_host(x["q"]), to_host(x["k_cache"]), to_host(x["v_cache"]), to_host(x["seqlens"]), w.scale)
+    first = _run(x, w.scale)
+    for _ in range(5):
+        assert torch.equal(_run(x, w.scale), first)
+    assert_parity(first, ref, torch.bfloat16, "decode")
+    kn = I.random_tensor((B, G, D), seed=7, dtype=torch.bfloat16, device=DEV)
+    vn = I.random_tensor((B, G, D), seed=8, dtype=torch.bfloat16, device=DEV)
+    outs = []
+    for _ in range(3):
+        kc, vc = x["k_cache"].clone(), x["v_cache"].clone()
+        torch.cuda.synchronize()
+        outs.append(gq.decode_step(x["q"], kc, vc, x["seqlens"], scale=w.scale, k_new=kn, v_new=vn))
+        torch.cuda.synchronize()
+    assert all(torch.equal(o, outs[0]) for o in outs[1:])
+    ref_a, _, _ = O.decode_step(to_host(x["q"]), to_host(x["k_cache"]), to_host(x["v_cache"]), to_host(x["seqlens"]),
+                                w.scale, k_new=to_host(kn), v_new=to_host(vn))
+    assert_parity(outs[0], ref_a, torch.bfloat16, "decode_step append")
