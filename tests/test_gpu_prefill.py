@@ -165,3 +165,19 @@ def test_prefill_fp16_full_size_sampled():
     ref = O.prefill(to_host(x["q"]), to_host(x["k"]), to_host(x["v"]), causal=True, rows=(rb, rt, rh))
     got = out[torch.as_tensor(rb), torch.as_tensor(rt), torch.as_tensor(rh)]
     assert_parity(got, ref, w.dtype, "fp16 rows")
+
+
+@pytest.mark.parametrize("H,G", [(12, 4), (10, 2), (30, 5), (21, 3), (96, 32)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_group_sizes_not_dividing_tile(H, G, causal):
+    """Group sizes r = H/G of 3, 5, 6 and 7 leave a 256-row query tile partly
+    unused (256 // r tokens of r heads), and r = 3 with d_h = 64; checked
+    against the oracle over every row, with a sequence length that ends in a
+    partial key tile."""
+    say(f"prefill r={H // G} H={H} G={G} causal={causal}")
+    D = 64 if H == 96 else 128
+    w = I.PrefillWorkload("r", 2, 301, H, G, D, torch.bfloat16, causal)
+    x = I.prefill_inputs(w, seed=H + G, device=DEV)
+    out = _run(x, causal)
+    ref = O.prefill(to_host(x["q"]), to_host(x["k"]), to_host(x["v"]), causal=causal)
+    assert_parity(out, ref, torch.bfloat16, f"r={H // G}")
