@@ -39,6 +39,9 @@ MUTANTS = [
      "int lo = (window > 0 && t + 1 > window) ? t - window : 0;"),
     ("prefill_window_scale", "double inv_sqrt_d = 1.0 / sqrt((double)D);", "double inv_sqrt_d = 1.0 / (double)D;"),
     ("weighted_pool_ignores_weights", "o[d] += w[i] * widen(in,", "o[d] += widen(in,"),
+    ("window_one_long", "int lo = (window > 0 && L > window) ? L - window : 0;",
+     "int lo = (window > 0 && L > window) ? L - window - 1 : 0;"),
+    ("append_value_not_written", "            memcpy((char *)v + dst, (const char *)v_new + (size_t)b * row, row);\n", ""),
 ]
 
 
