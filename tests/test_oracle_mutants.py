@@ -42,6 +42,10 @@ MUTANTS = [
     ("window_one_long", "int lo = (window > 0 && L > window) ? L - window : 0;",
      "int lo = (window > 0 && L > window) ? L - window - 1 : 0;"),
     ("append_value_not_written", "            memcpy((char *)v + dst, (const char *)v_new + (size_t)b * row, row);\n", ""),
+    ("no_max_subtraction", "s[t] = exp(s[t] - m);", "s[t] = exp(s[t]);"),
+    ("max_of_first_key_only", "if (s[t] > m)\n            m = s[t];", "if (t == 0)\n            m = s[t];"),
+    ("pool_strided_groups", "if (oracle_group_of_head(i, H, G) != g)\n                    continue;\n                ++members;",
+     "if (i % G != g)\n                    continue;\n                ++members;"),
 ]
 
 
