@@ -19,7 +19,8 @@ import os
 
 import torch
 
-__all__ = ["GqaError", "decode", "prefill", "mean_pool_kv", "decode_plan", "library_path", "load_library"]
+__all__ = ["GqaError", "decode", "decode_step", "prefill", "mean_pool_kv", "weighted_pool_kv", "decode_plan",
+           "release_workspaces", "library_path", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libgqa.so")
@@ -64,8 +65,12 @@ def load_library():
         getattr(lib, fn).restype = i32
     lib.gqa_status_string.argtypes = [i32]
     lib.gqa_status_string.restype = ctypes.c_char_p
+    lib.gqa_last_hip_error.argtypes = []
+    lib.gqa_last_hip_error.restype = ctypes.c_char_p
     lib.gqa_last_error.argtypes = []
     lib.gqa_last_error.restype = ctypes.c_char_p
+    lib.gqa_release_workspaces.argtypes = []
+    lib.gqa_release_workspaces.restype = i32
     lib.gqa_abi_version.argtypes = []
     lib.gqa_abi_version.restype = i32
     _lib = lib
@@ -75,7 +80,7 @@ def load_library():
 def _check(status: int):
     if status != GQA_OK:
         lib = load_library()
-        raise GqaError(status, lib.gqa_last_error().decode() or lib.gqa_status_string(status).decode())
+        raise GqaError(status, lib.gqa_last_hip_error().decode() or lib.gqa_status_string(status).decode())
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -226,6 +231,12 @@ def weighted_pool_kv(x, weights, G: int, out=None):
         _check(lib.gqa_weighted_pool_kv(x.data_ptr(), weights.data_ptr(), N, H, G, D, _dtype_code(x),
                                         out.data_ptr(), _stream_ptr(dev)))
     return out
+
+
+def release_workspaces():
+    """Free every decode workspace the library holds (waits for the devices
+    first). Graphs captured earlier must not be replayed afterwards."""
+    _check(load_library().gqa_release_workspaces())
 
 
 def decode_plan(B, H, G, D, Tmax, dtype=torch.bfloat16, split_tokens=0, cu_count=256):

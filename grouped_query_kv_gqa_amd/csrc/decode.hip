@@ -703,10 +703,10 @@ decode_f32_kernel(const float *__restrict__ q, float *kc, float *vc, const float
     }
 }
 
-template <int D, int NT, int WAVES, int GB>
+template <typename T, int D, int NT, int WAVES, int GB, bool APPEND>
 const void *split_symbol()
 {
-    return reinterpret_cast<const void *>(&decode_split_kernel<__bf16, D, NT, WAVES, GB, false>);
+    return reinterpret_cast<const void *>(&decode_split_kernel<T, D, NT, WAVES, GB, APPEND>);
 }
 
 // 16-bit storage of type T; the pointers carry its raw bit patterns.
@@ -752,10 +752,16 @@ hipError_t with_variant(const DecodePlan &p, int D, F &&f)
 
 }  // namespace
 
-hipError_t decode_blocks_per_cu(const DecodePlan &p, int D, int *blocks)
+hipError_t decode_blocks_per_cu(const DecodePlan &p, int D, gqa_dtype dtype, bool append, int *blocks)
 {
     return with_variant(p, D, [&]<int DD, int NTT, int WW, int GG>() {
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, split_symbol<DD, NTT, WW, GG>(), WW * 64, 0);
+        const void *f;
+        if (dtype == GQA_FP16)
+            f = append ? split_symbol<_Float16, DD, NTT, WW, GG, true>()
+                       : split_symbol<_Float16, DD, NTT, WW, GG, false>();
+        else
+            f = append ? split_symbol<__bf16, DD, NTT, WW, GG, true>() : split_symbol<__bf16, DD, NTT, WW, GG, false>();
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, f, WW * 64, 0);
     });
 }
 

@@ -3,7 +3,8 @@
 // Every entry point checks its arguments on the host (plan.cpp) before it
 // touches the HIP runtime, then queues its kernels on the caller's stream.
 // The only state the library keeps is the split-decode workspace, one per
-// (device, stream), grown on demand with stream-ordered allocation.
+// (device, stream), grown on demand with stream-ordered allocation (policy in
+// workspace.cpp), and cached device properties.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -13,6 +14,7 @@
 #include "gqa.h"
 #include "kernels.h"
 #include "plan.h"
+#include "workspace.h"
 
 namespace {
 
@@ -30,28 +32,57 @@ gqa_status hip_failure(hipError_t e, const char *where)
     return GQA_ERR_HIP;
 }
 
-struct Workspace {
-    char *ptr = nullptr;
-    int64_t bytes = 0;
-};
-
-struct Key {
-    int device;
-    hipStream_t stream;
-    bool operator==(const Key &o) const { return device == o.device && stream == o.stream; }
-};
-
-struct KeyHash {
-    size_t operator()(const Key &k) const
+// Device calls of the workspace registry, through the HIP runtime.
+struct HipBackend final : gqa::WsBackend {
+    int alloc(void **ptr, int64_t bytes, void *stream) override
     {
-        return std::hash<void *>()(static_cast<void *>(k.stream)) * 31u + static_cast<size_t>(k.device);
+        return hipMallocAsync(ptr, static_cast<size_t>(bytes), static_cast<hipStream_t>(stream));
     }
+    int free_async(void *ptr, void *stream) override
+    {
+        return hipFreeAsync(ptr, static_cast<hipStream_t>(stream));
+    }
+    int free_now(int device, void *ptr) override
+    {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != device)
+            e = hipSetDevice(device);
+        if (e == hipSuccess)
+            e = hipFreeAsync(ptr, nullptr);
+        if (e == hipSuccess)
+            e = hipStreamSynchronize(nullptr);
+        if (cur != device)
+            (void)hipSetDevice(cur);
+        return e;
+    }
+    int sync_device(int device) override
+    {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != device)
+            e = hipSetDevice(device);
+        if (e == hipSuccess)
+            e = hipDeviceSynchronize();
+        if (cur != device)
+            (void)hipSetDevice(cur);
+        return e;
+    }
+    int is_capturing(void *stream, bool *capturing) override
+    {
+        hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+        hipError_t e = hipStreamIsCapturing(static_cast<hipStream_t>(stream), &st);
+        *capturing = st != hipStreamCaptureStatusNone;
+        return e;
+    }
+    std::string error_text(int code) override { return hipGetErrorString(static_cast<hipError_t>(code)); }
 };
 
 std::mutex g_mutex;
-std::unordered_map<Key, Workspace, KeyHash> g_workspaces;
+HipBackend g_backend;
+gqa::WorkspaceRegistry g_workspaces(&g_backend);
 std::unordered_map<int, int> g_cu_count;
-std::unordered_map<int64_t, int> g_blocks_per_cu;  // (device, d_h, nt, waves, gb) -> workgroups per CU
+std::unordered_map<int64_t, int> g_blocks_per_cu;  // variant key -> workgroups per CU
 
 gqa_status cu_count(int device, int *out)
 {
@@ -69,16 +100,17 @@ gqa_status cu_count(int device, int *out)
     return GQA_OK;
 }
 
-gqa_status blocks_per_cu(int device, const gqa::DecodePlan &p, int d_h, int *out)
+gqa_status blocks_per_cu(int device, const gqa::DecodePlan &p, int d_h, gqa_dtype dtype, bool append, int *out)
 {
-    const int64_t key = ((((int64_t)device * 256 + d_h) * 8 + p.nt) * 16 + p.waves) * 16 + p.gb;
+    const int64_t key =
+        ((((((int64_t)device * 256 + d_h) * 8 + p.nt) * 16 + p.waves) * 16 + p.gb) * 4 + (int)dtype) * 2 + append;
     auto it = g_blocks_per_cu.find(key);
     if (it != g_blocks_per_cu.end()) {
         *out = it->second;
         return GQA_OK;
     }
     int n = 0;
-    hipError_t e = gqa::decode_blocks_per_cu(p, d_h, &n);
+    hipError_t e = gqa::decode_blocks_per_cu(p, d_h, dtype, append, &n);
     if (e != hipSuccess)
         return hip_failure(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     if (n < 1)
@@ -88,38 +120,14 @@ gqa_status blocks_per_cu(int device, const gqa::DecodePlan &p, int d_h, int *out
     return GQA_OK;
 }
 
-// A workspace of at least `bytes` for this (device, stream). Growth frees the
-// old block in stream order, so work already queued on the stream still sees
-// valid memory.
-gqa_status workspace_for(int device, hipStream_t stream, int64_t bytes, char **out)
-{
-    Workspace &ws = g_workspaces[Key{device, stream}];
-    if (ws.bytes < bytes) {
-        hipError_t e;
-        if (ws.ptr) {
-            e = hipFreeAsync(ws.ptr, stream);
-            if (e != hipSuccess)
-                return hip_failure(e, "hipFreeAsync");
-            ws.ptr = nullptr;
-            ws.bytes = 0;
-        }
-        const int64_t grown = bytes + bytes / 4;  // headroom for growth
-        e = hipMallocAsync(reinterpret_cast<void **>(&ws.ptr), static_cast<size_t>(grown), stream);
-        if (e != hipSuccess)
-            return hip_failure(e, "hipMallocAsync");
-        ws.bytes = grown;
-    }
-    *out = ws.ptr;
-    return GQA_OK;
-}
-
 }  // namespace
 
 namespace {
 
 gqa_status decode_impl(const void *q, const void *k_new, const void *v_new, const void *k_cache,
                        const void *v_cache, const int32_t *seqlens, int B, int H, int G, int d_h, int Tmax,
-                       float scale, int window, int split_tokens, gqa_dtype dtype, void *out, hipStream_t stream)
+                       float scale, int window, int split_tokens, gqa_dtype dtype, void *out, hipStream_t stream,
+                       char *fixed_ws, int64_t fixed_ws_bytes)
 {
     std::string err;
     gqa_status s = gqa::check_decode_step(q, k_new, v_new, k_cache, v_cache, seqlens, B, H, G, d_h, Tmax, scale,
@@ -128,12 +136,12 @@ gqa_status decode_impl(const void *q, const void *k_new, const void *v_new, cons
         return record(s, err);
     if (split_tokens < 0)
         return record(GQA_ERR_INVALID_ARG, "split_tokens must be >= 0");
+    gqa::DecodePlan plan;
+    // sizes and launch limits, before anything touches the runtime
+    if ((s = gqa::plan_decode(B, H, G, d_h, Tmax, dtype, split_tokens, 0, 0, &plan, &err)) != GQA_OK)
+        return record(s, err);
     if (B == 0)
         return GQA_OK;
-    if (B > 65535 || (int64_t)B * H > 0x7fffffff)
-        return record(GQA_ERR_UNSUPPORTED, "B must be <= 65535");
-    if ((int64_t)B * Tmax > 0x7fffffff)
-        return record(GQA_ERR_UNSUPPORTED, "B * Tmax must be below 2^31");
 
     std::lock_guard<std::mutex> lock(g_mutex);
     int device = 0;
@@ -143,23 +151,26 @@ gqa_status decode_impl(const void *q, const void *k_new, const void *v_new, cons
     int cus = 0;
     if ((s = cu_count(device, &cus)) != GQA_OK)
         return s;
-    gqa::DecodePlan plan;
-    if ((s = gqa::plan_decode(B, H, G, d_h, Tmax, dtype, split_tokens, cus, 0, &plan, &err)) != GQA_OK)
-        return record(s, err);
-    if ((int64_t)(G / plan.gb) * plan.head_tiles > 65535)
-        return record(GQA_ERR_UNSUPPORTED, "too many key/value heads");
-
+    const bool append = k_new != nullptr;
     gqa::DecodeArgs a{q, k_cache, v_cache, k_new, v_new, seqlens, B, H, G, d_h, Tmax, window, scale,
                       out, nullptr, nullptr, stream};
     if (dtype != GQA_FP32) {
         int bpc = 0;
-        if ((s = blocks_per_cu(device, plan, d_h, &bpc)) != GQA_OK)
+        if ((s = blocks_per_cu(device, plan, d_h, dtype, append, &bpc)) != GQA_OK)
             return s;
         if ((s = gqa::plan_decode(B, H, G, d_h, Tmax, dtype, split_tokens, cus, bpc, &plan, &err)) != GQA_OK)
             return record(s, err);
         char *ws = nullptr;
-        if ((s = workspace_for(device, stream, plan.workspace_bytes, &ws)) != GQA_OK)
-            return s;
+        if (fixed_ws) {
+            if (plan.workspace_bytes > fixed_ws_bytes)
+                return record(GQA_ERR_UNSUPPORTED,
+                              "this decode needs " + std::to_string(plan.workspace_bytes) +
+                                  " bytes of scratch, above the fixed maximum of " + std::to_string(fixed_ws_bytes));
+            ws = fixed_ws;
+        } else {
+            if ((s = g_workspaces.get(device, stream, plan.workspace_bytes, &ws, &err)) != GQA_OK)
+                return record(s, err);
+        }
         a.part = reinterpret_cast<float *>(ws + plan.part_offset);
         a.lse = reinterpret_cast<float *>(ws + plan.lse_offset);
     }
@@ -173,13 +184,12 @@ gqa_status decode_impl(const void *q, const void *k_new, const void *v_new, cons
 
 extern "C" {
 
-
 gqa_status gqa_decode_ex(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens, int B,
                          int H, int G, int d_h, int Tmax, float scale, gqa_dtype dtype, void *out,
                          hipStream_t stream, int split_tokens)
 {
     return decode_impl(q, nullptr, nullptr, k_cache, v_cache, seqlens, B, H, G, d_h, Tmax, scale, 0, split_tokens,
-                       dtype, out, stream);
+                       dtype, out, stream, nullptr, 0);
 }
 
 gqa_status gqa_decode_step(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
@@ -187,7 +197,7 @@ gqa_status gqa_decode_step(const void *q, const void *k_new, const void *v_new, 
                            int split_tokens, gqa_dtype dtype, void *out, hipStream_t stream)
 {
     return decode_impl(q, k_new, v_new, k_cache, v_cache, seqlens, B, H, G, d_h, Tmax, scale, window, split_tokens,
-                       dtype, out, stream);
+                       dtype, out, stream, nullptr, 0);
 }
 
 gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens, int B,
@@ -209,8 +219,8 @@ gqa_status gqa_prefill_ex(const void *q, const void *k, const void *v, int B, in
         return record(GQA_ERR_INVALID_ARG, "a sliding window needs causal = 1");
     if (B == 0 || T == 0)
         return GQA_OK;
-    if ((int64_t)B * T * H > 0x7fffffff)
-        return record(GQA_ERR_UNSUPPORTED, "B*T*H must fit in 31 bits");
+    if ((s = gqa::check_prefill_launch(B, T, H, G, d_h, dtype, &err)) != GQA_OK)
+        return record(s, err);
     gqa::PrefillArgs a{q, k, v, B, T, H, G, d_h, causal, window, out, stream};
     hipError_t e = gqa::launch_prefill(a, dtype);
     if (e != hipSuccess)
@@ -287,14 +297,29 @@ const char *gqa_status_string(gqa_status s)
     return "unknown status";
 }
 
+const char *gqa_last_hip_error(void)
+{
+    return g_last_error.c_str();
+}
+
 const char *gqa_last_error(void)
 {
     return g_last_error.c_str();
 }
 
+gqa_status gqa_release_workspaces(void)
+{
+    std::lock_guard<std::mutex> lock(g_mutex);
+    std::string err;
+    gqa_status s = g_workspaces.release_all(&err);
+    if (s != GQA_OK)
+        return record(s, err);
+    return GQA_OK;
+}
+
 int gqa_abi_version(void)
 {
-    return 1;
+    return 2;
 }
 
 }  // extern "C"

@@ -22,8 +22,9 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodePlan &plan, const DecodeArgs &args, gqa_dtype dtype);
 
-// Workgroups of the plan's bf16 decode variant that fit on one compute unit.
-hipError_t decode_blocks_per_cu(const DecodePlan &plan, int d_h, int *blocks);
+// Workgroups of the plan's 16-bit decode variant (storage type, append or
+// not) that fit on one compute unit.
+hipError_t decode_blocks_per_cu(const DecodePlan &plan, int d_h, gqa_dtype dtype, bool append, int *blocks);
 
 struct PrefillArgs {
     const void *q, *k, *v;

@@ -155,13 +155,25 @@ gqa_status plan_decode(int B, int H, int G, int d_h, int Tmax, gqa_dtype dtype, 
             break;
         }
     }
+    // Launch limits, checked here so that gqa_decode_plan and gqa_decode
+    // agree: the merge grid has one row of workgroups per sequence (at most
+    // 65535), flat positions are 32-bit on the device, and a launch holds
+    // fewer than 2^32 work-items along x.
+    if (B > 65535)
+        return fail(err, GQA_ERR_UNSUPPORTED, "B must be <= 65535");
+    if ((int64_t)B * Tmax > 0x7fffffff)
+        return fail(err, GQA_ERR_UNSUPPORTED, "B * Tmax must be below 2^31");
     if (dtype == GQA_FP32 || B == 0) {
+        if ((int64_t)B * H * 64 > 0xffffffffLL)
+            return fail(err, GQA_ERR_UNSUPPORTED, "B * H must be below 2^26 on the fp32 path");
         p.nwg = 0;
         if (plan)
             *plan = p;
         return GQA_OK;
     }
     const int64_t combos = (int64_t)(G / p.gb) * p.head_tiles;
+    if (combos > 65535)
+        return fail(err, GQA_ERR_UNSUPPORTED, "too many key/value heads");
     const int64_t positions = (int64_t)B * Tmax;
     const int64_t max_pieces = ceil_div(positions > 0 ? positions : 1, kDecodeTile);
     int64_t nwg;
@@ -180,7 +192,7 @@ gqa_status plan_decode(int B, int H, int G, int d_h, int Tmax, gqa_dtype dtype, 
         int64_t P = round_up(ceil_div(positions > 0 ? positions : 1, nwg), kDecodeTile);
         p.full_P = (int)(P < kDecodeTile ? kDecodeTile : P);
     }
-    if (nwg > 0x7fffffff)
+    if (nwg * p.waves * 64 > 0xffffffffLL)
         return fail(err, GQA_ERR_UNSUPPORTED, "too many cache positions for the split size");
     p.nwg = (int)nwg;
     // Merge layout: enough slot lanes that each takes at most 4 pieces of a
@@ -233,6 +245,23 @@ gqa_status check_prefill(const void *q, const void *k, const void *v, int B, int
     if (ranges_overlap(out, q_bytes, q, q_bytes) || ranges_overlap(out, q_bytes, k, kv_bytes) ||
         ranges_overlap(out, q_bytes, v, kv_bytes))
         return fail(err, GQA_ERR_INVALID_ARG, "out overlaps an input");
+    return GQA_OK;
+}
+
+gqa_status check_prefill_launch(int B, int T, int H, int G, int d_h, gqa_dtype dtype, std::string *err)
+{
+    // grid y = G and z = B (each at most 65535); fewer than 2^32 work-items
+    // along x; 31-bit row indices inside the kernels.
+    if (B > 65535 || G > 65535)
+        return fail(err, GQA_ERR_UNSUPPORTED, "B and G must be <= 65535");
+    const int64_t rows = (int64_t)B * T * H;
+    if (rows > 0x7fffffff)
+        return fail(err, GQA_ERR_UNSUPPORTED, "B * T * H must be below 2^31");
+    const int r = H / G;
+    const bool row_kernel = dtype == GQA_FP32 || r > kPrefillRows;
+    if (row_kernel && rows * 64 > 0xffffffffLL)
+        return fail(err, GQA_ERR_UNSUPPORTED, "B * T * H must be below 2^26 on the row-per-wave path");
+    (void)d_h;
     return GQA_OK;
 }
 

@@ -49,6 +49,9 @@ gqa_status check_decode_step(const void *q, const void *k_new, const void *v_new
 
 gqa_status check_prefill(const void *q, const void *k, const void *v, int B, int T, int H, int G, int d_h,
                          int causal, gqa_dtype dtype, const void *out, std::string *err);
+// Grid and index limits of the prefill launch (after check_prefill).
+constexpr int kPrefillRows = 256;  // query rows (token x head) per MFMA prefill workgroup
+gqa_status check_prefill_launch(int B, int T, int H, int G, int d_h, gqa_dtype dtype, std::string *err);
 gqa_status check_mean_pool(const void *in, int64_t N, int H, int G, int d_h, gqa_dtype dtype,
                            const void *out, std::string *err);
 

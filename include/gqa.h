@@ -31,7 +31,7 @@
  *   - A batch of zero sequences (B = 0, or N = 0 for pooling) is valid and
  *     queues nothing; its pointers may be NULL.
  *   - GQA_ERR_HIP means the HIP runtime reported an error while queueing;
- *     gqa_last_error() then holds its text.
+ *     gqa_last_hip_error() then holds its text.
  *   - Thread safety: calls may be made from several host threads. Calls that
  *     share a stream are serialised by that stream.
  */
@@ -50,7 +50,7 @@ typedef enum gqa_status {
     GQA_OK = 0,
     GQA_ERR_INVALID_ARG = 1, /* null pointer, negative size, G not dividing H, misalignment, aliasing */
     GQA_ERR_UNSUPPORTED = 2, /* valid but not built: d_h other than 64 or 128, unknown dtype */
-    GQA_ERR_HIP = 3          /* the HIP runtime failed; see gqa_last_error() */
+    GQA_ERR_HIP = 3          /* the HIP runtime failed; see gqa_last_hip_error() */
 } gqa_status;
 
 typedef enum gqa_dtype { GQA_BF16 = 0, GQA_FP32 = 1, GQA_FP16 = 2 } gqa_dtype;
@@ -79,14 +79,27 @@ typedef enum gqa_dtype { GQA_BF16 = 0, GQA_FP32 = 1, GQA_FP16 = 2 } gqa_dtype;
  * Work is balanced over the GPU by laying all sequences' cache positions
  * end to end and giving every workgroup an equal slice; a sequence cut over
  * several slices is merged with a log-sum-exp combine in a second launch on
- * the same stream. The fp32 partial rows live in a library-owned workspace,
- * one per (device, stream), allocated with stream-ordered allocation on first
- * use, grown when needed, and kept until the process ends. Results are
- * bit-identical from call to call. Graph capture: make one call of the same
- * (or a larger) shape on the capture stream before capturing, so that the
- * captured calls find the workspace and allocate nothing; the captured graph
- * then reads seqlens and the tensors at replay time.
- * Requires 1 <= G, G divides H, Tmax >= 0, d_h in {64, 128}.
+ * the same stream. Results are bit-identical from call to call.
+ *
+ * Workspace. The fp32 partial rows live in a library-owned block of device
+ * memory, one per (device, stream): allocated with stream-ordered allocation
+ * (hipMallocAsync on `stream`) by the first 16-bit call that needs it and
+ * replaced by a larger one when a later call needs more. Calls on one stream
+ * are ordered by that stream; calls on different streams use different
+ * blocks. gqa_release_workspaces() frees them all.
+ *
+ * Graph capture. A call made while `stream` is being captured never
+ * allocates: if the stream's workspace is missing or too small it returns
+ * GQA_ERR_INVALID_ARG and queues nothing, so make one eager call of the same
+ * (or a larger) shape on the capture stream first. The captured graph keeps
+ * the block's address and reads seqlens and the tensors at replay time. A
+ * block that a captured graph references is never freed when a later, larger
+ * eager call replaces it (it is kept until gqa_release_workspaces), so the
+ * graph stays valid. The graph shares the block with every other call on
+ * its capture stream: replaying it while such a call (or another graph
+ * captured on that stream) runs on a different stream races.
+ * Requires 1 <= G, G divides H, Tmax >= 0, d_h in {64, 128}; B <= 65535 and
+ * B * Tmax < 2^31 (else GQA_ERR_UNSUPPORTED).
  */
 gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens,
                       int B, int H, int G, int d_h, int Tmax, float scale, gqa_dtype dtype, void *out,
@@ -193,7 +206,8 @@ gqa_status gqa_mean_pool_kv(const void *in, int64_t N, int H, int G, int d_h, gq
  * shrink the slice on the device), and the workspace bytes. For the fp32
  * path: chunk_tokens = Tmax, num_splits = 1, workspace 0. `cu_count` is the
  * GPU's compute-unit count (256 on MI355X). Any output pointer may be NULL.
- * Returns GQA_OK or the status gqa_decode would return for the same sizes.
+ * Returns GQA_OK or the status gqa_decode would return for the same sizes
+ * (the size and launch-limit checks are shared).
  */
 gqa_status gqa_decode_plan(int B, int H, int G, int d_h, int Tmax, gqa_dtype dtype, int split_tokens,
                            int cu_count, int *chunk_tokens, int *num_splits, int64_t *workspace_bytes);
@@ -217,10 +231,23 @@ gqa_status gqa_weighted_pool_kv(const void *in, const float *weights, int64_t N,
 /* Short constant text for a status code. */
 const char *gqa_status_string(gqa_status s);
 
-/* Text of the last failure on the calling thread ("" if none). */
+/* Text of the last failure on the calling thread ("" if none): the HIP
+ * runtime's message after GQA_ERR_HIP, the failed check otherwise. */
+const char *gqa_last_hip_error(void);
+
+/* The same text as gqa_last_hip_error (older name, kept). */
 const char *gqa_last_error(void);
 
-/* Library ABI version: 1. */
+/*
+ * gqa_release_workspaces -- free every decode workspace the library holds
+ * (on every device and stream, including blocks kept alive for captured
+ * graphs), after waiting for the devices that hold them to go idle. Graphs
+ * captured before this call must not be replayed after it; no other library
+ * call may run concurrently. The next decode call allocates afresh.
+ */
+gqa_status gqa_release_workspaces(void);
+
+/* Library ABI version: 2. */
 int gqa_abi_version(void);
 
 #ifdef __cplusplus

@@ -22,7 +22,8 @@ def _declared():
 def test_header_symbols_exported():
     names = _declared()
     assert {"gqa_decode", "gqa_decode_ex", "gqa_prefill", "gqa_mean_pool_kv", "gqa_decode_plan",
-            "gqa_status_string", "gqa_last_error", "gqa_abi_version"} <= set(names)
+            "gqa_status_string", "gqa_last_hip_error", "gqa_last_error", "gqa_release_workspaces",
+            "gqa_abi_version"} <= set(names)
     lib = ctypes.CDLL(gq.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -37,7 +38,7 @@ def test_status_strings():
     assert lib.gqa_status_string(1) == b"invalid argument"
     assert lib.gqa_status_string(2) == b"unsupported"
     assert lib.gqa_status_string(3) == b"HIP runtime error"
-    assert lib.gqa_abi_version() == 1
+    assert lib.gqa_abi_version() == 2
 
 
 def _decode(lib, **kw):
@@ -50,7 +51,8 @@ def _decode(lib, **kw):
 def test_decode_argument_checks():
     lib = gq.load_library()
     assert _decode(lib, G=3) == gq.GQA_ERR_INVALID_ARG
-    assert b"divide" in lib.gqa_last_error()
+    assert b"divide" in lib.gqa_last_hip_error()
+    assert lib.gqa_last_error() == lib.gqa_last_hip_error()
     assert _decode(lib, H=0) == gq.GQA_ERR_INVALID_ARG
     assert _decode(lib, B=-1) == gq.GQA_ERR_INVALID_ARG
     assert _decode(lib, T=-1) == gq.GQA_ERR_INVALID_ARG
@@ -60,9 +62,9 @@ def test_decode_argument_checks():
     assert _decode(lib, q=None) == gq.GQA_ERR_INVALID_ARG
     assert _decode(lib, sl=None) == gq.GQA_ERR_INVALID_ARG
     assert _decode(lib, q=18) == gq.GQA_ERR_INVALID_ARG          # misaligned
-    assert b"aligned" in lib.gqa_last_error()
+    assert b"aligned" in lib.gqa_last_hip_error()
     assert _decode(lib, out=48) == gq.GQA_ERR_INVALID_ARG         # out aliases v
-    assert b"overlaps" in lib.gqa_last_error()
+    assert b"overlaps" in lib.gqa_last_hip_error()
     assert _decode(lib, split=-5) == gq.GQA_ERR_INVALID_ARG
     assert _decode(lib, B=0, q=None, k=None, v=None, sl=None, out=None) == gq.GQA_OK  # empty batch
 
@@ -97,6 +99,13 @@ def test_decode_plan():
     # fp32 never splits
     import torch
     assert gq.decode_plan(1, 8, 2, 64, 256, dtype=torch.float32) == (256, 1, 0)
+    # the plan applies the same size limits as the decode call
+    for args in [(65536, 8, 2, 128, 16), (2, 8, 2, 128, 1 << 30)]:
+        with pytest.raises(gq.GqaError) as e:
+            gq.decode_plan(*args)
+        assert e.value.status == gq.GQA_ERR_UNSUPPORTED
+        assert _decode(gq.load_library(), B=args[0], T=args[4], q=1 << 40, k=2 << 40, v=3 << 40, sl=4 << 40,
+                       out=5 << 40) == gq.GQA_ERR_UNSUPPORTED
 
 
 def test_host_plan_sanitized(tmp_path):
@@ -121,6 +130,21 @@ int main() {
     }
   }
   assert(gqa::plan_decode(1, 6, 4, 128, 10, GQA_BF16, 0, 256, 0, &p, &e) == GQA_ERR_INVALID_ARG);
+  // launch limits: merge grid rows, 31-bit flat positions, 2^32 work-items
+  assert(gqa::plan_decode(65535, 8, 2, 128, 16, GQA_BF16, 0, 256, 0, &p, &e) == GQA_OK);
+  assert(gqa::plan_decode(65536, 8, 2, 128, 16, GQA_BF16, 0, 256, 0, &p, &e) == GQA_ERR_UNSUPPORTED);
+  assert(gqa::plan_decode(65536, 8, 2, 128, 16, GQA_FP32, 0, 256, 0, &p, &e) == GQA_ERR_UNSUPPORTED);
+  assert(gqa::plan_decode(2, 8, 2, 128, 1 << 30, GQA_BF16, 0, 256, 0, &p, &e) == GQA_ERR_UNSUPPORTED);
+  assert(gqa::plan_decode(1, 8, 2, 128, 1 << 30, GQA_BF16, 0, 256, 0, &p, &e) == GQA_OK);
+  assert(gqa::plan_decode(1, 8, 2, 128, 1 << 30, GQA_BF16, 32, 256, 0, &p, &e) == GQA_ERR_UNSUPPORTED);
+  assert(gqa::plan_decode(1, 8, 2, 128, 1 << 30, GQA_BF16, 4096, 256, 0, &p, &e) == GQA_OK);
+  assert(gqa::plan_decode(65535, 2048, 2, 128, 1, GQA_FP32, 0, 256, 0, &p, &e) == GQA_ERR_UNSUPPORTED);
+  assert(gqa::check_prefill_launch(65535, 8, 8, 2, 128, GQA_BF16, &e) == GQA_OK);
+  assert(gqa::check_prefill_launch(65536, 8, 8, 2, 128, GQA_BF16, &e) == GQA_ERR_UNSUPPORTED);
+  assert(gqa::check_prefill_launch(1, 1 << 24, 64, 8, 128, GQA_BF16, &e) == GQA_OK);
+  assert(gqa::check_prefill_launch(1, 1 << 24, 128, 8, 128, GQA_BF16, &e) == GQA_ERR_UNSUPPORTED);
+  assert(gqa::check_prefill_launch(1, 1 << 21, 64, 8, 128, GQA_FP32, &e) == GQA_ERR_UNSUPPORTED);
+  assert(gqa::check_prefill_launch(1, 1 << 19, 64, 8, 128, GQA_FP32, &e) == GQA_OK);
   char buf[64];
   assert(gqa::check_decode(buf, buf + 16, buf + 32, (const int32_t*)buf, 1, 8, 2, 128, 1, 1.f, GQA_BF16, buf, &e) == GQA_ERR_INVALID_ARG);
   std::puts("ok");
@@ -134,3 +158,84 @@ int main() {
                     "-o", str(exe)], check=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and "ok" in r.stdout, r.stderr
+
+
+def test_workspace_registry_sanitized(tmp_path):
+    """The decode workspace policy (allocate, grow, never allocate or free a
+    graph's block during or after capture, release everything on request),
+    built host-only with g++ under ASan/UBSan against a fake device whose
+    blocks are host allocations: a block used past its size, freed twice or
+    never freed fails the sanitizer."""
+    src = tmp_path / "w.cpp"
+    src.write_text(r'''
+#include "workspace.h"
+#include <cassert>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <set>
+struct Fake : gqa::WsBackend {
+  std::set<void*> live; int allocs = 0, async_frees = 0, now_frees = 0, syncs = 0;
+  bool capturing = false, fail_alloc = false;
+  int alloc(void **p, int64_t bytes, void *) override {
+    if (fail_alloc) return 2;
+    *p = std::malloc((size_t)bytes); live.insert(*p); ++allocs; return 0; }
+  int free_async(void *p, void *) override { assert(live.erase(p) == 1); std::free(p); ++async_frees; return 0; }
+  int free_now(int, void *p) override { assert(live.erase(p) == 1); std::free(p); ++now_frees; return 0; }
+  int sync_device(int) override { ++syncs; return 0; }
+  int is_capturing(void *, bool *c) override { *c = capturing; return 0; }
+  std::string error_text(int c) override { return "fake error " + std::to_string(c); }
+};
+int main() {
+  Fake f; gqa::WorkspaceRegistry reg(&f); std::string e; char *p = nullptr, *q = nullptr;
+  void *s1 = (void*)0x10, *s2 = (void*)0x20;
+  // nothing needed: nothing allocated
+  assert(reg.get(0, s1, 0, &p, &e) == GQA_OK && p == nullptr && f.allocs == 0);
+  // first use allocates; the whole requested size is usable
+  assert(reg.get(0, s1, 1000, &p, &e) == GQA_OK && p && f.allocs == 1);
+  std::memset(p, 1, 1000);
+  // smaller and equal requests reuse the block
+  assert(reg.get(0, s1, 500, &q, &e) == GQA_OK && q == p && f.allocs == 1);
+  assert(reg.get(0, s1, 1000, &q, &e) == GQA_OK && q == p && f.allocs == 1);
+  // another stream or device gets its own block
+  assert(reg.get(0, s2, 1000, &q, &e) == GQA_OK && q != p && f.allocs == 2);
+  assert(reg.get(1, s1, 1000, &q, &e) == GQA_OK && f.allocs == 3 && reg.live_count() == 3);
+  // growth without capture frees the old block in stream order
+  assert(reg.get(0, s1, 5000, &q, &e) == GQA_OK && q != p && f.allocs == 4 && f.async_frees == 1);
+  std::memset(q, 2, 5000);
+  p = q;
+  // a failed allocation keeps the old block
+  f.fail_alloc = true;
+  assert(reg.get(0, s1, 100000, &q, &e) == GQA_ERR_HIP && e.find("fake error") != std::string::npos);
+  f.fail_alloc = false;
+  assert(reg.get(0, s1, 5000, &q, &e) == GQA_OK && q == p);
+  // during capture: a block that fits is used and marked, nothing allocated
+  f.capturing = true;
+  assert(reg.get(0, s1, 4000, &q, &e) == GQA_OK && q == p && reg.live_captured(0, s1) && f.allocs == 4);
+  // during capture: too small or missing is an error, nothing allocated or freed
+  assert(reg.get(0, s1, 1 << 20, &q, &e) == GQA_ERR_INVALID_ARG && e.find("captur") != std::string::npos);
+  assert(reg.get(2, s1, 10, &q, &e) == GQA_ERR_INVALID_ARG && f.allocs == 4 && f.async_frees == 1);
+  assert(reg.live_bytes(0, s1) >= 5000);
+  f.capturing = false;
+  // growth after capture retires the graph's block instead of freeing it
+  assert(reg.get(0, s1, 20000, &q, &e) == GQA_OK && q != p && f.async_frees == 1 && reg.retired_count() == 1);
+  assert(f.live.count(p) == 1 && !reg.live_captured(0, s1));
+  std::memset(p, 3, 5000);  // the retired block is still valid memory
+  std::memset(q, 4, 20000);
+  // release frees everything after waiting for both devices
+  assert(reg.release_all(&e) == GQA_OK && f.live.empty() && f.syncs == 2);
+  assert(reg.live_count() == 0 && reg.retired_count() == 0);
+  // and the next call allocates afresh
+  assert(reg.get(0, s1, 64, &q, &e) == GQA_OK && f.allocs == 6);
+  assert(reg.release_all(&e) == GQA_OK && f.live.empty());
+  std::puts("ok");
+  return 0;
+}
+''')
+    exe = tmp_path / "w"
+    csrc = os.path.join(ROOT, "grouped_query_kv_gqa_amd", "csrc")
+    subprocess.run(["g++", "-std=c++20", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                    f"-I{csrc}", f"-I{os.path.join(ROOT, 'include')}", str(src), os.path.join(csrc, "workspace.cpp"),
+                    "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stdout + r.stderr

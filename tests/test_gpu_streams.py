@@ -80,3 +80,51 @@ def test_graph_capture_decode_and_prefill():
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"decode replay {rep}"
         assert torch.equal(pout, pref), f"prefill replay {rep}"
+
+
+def test_graph_survives_workspace_growth():
+    """A decode captured at a small shape keeps working after a larger eager
+    call on the capture stream replaces the stream's workspace: the captured
+    block is kept alive, and every replay matches the eager result bit for
+    bit. A capture on a stream whose workspace is missing fails cleanly
+    without allocating."""
+    say("graph replay after workspace growth on the capture stream")
+    small = I.DecodeWorkload("small", 4, 32, 8, 128, 1024, torch.bfloat16, ragged=(1, 1024))
+    big = I.DecodeWorkload("big", 32, 64, 8, 128, 4096, torch.bfloat16, ragged=(1024, 4096))
+    x = I.decode_inputs(small, seed=51, device=DEV)
+    xb = I.decode_inputs(big, seed=52, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _decode(x, small)  # sizes the stream's workspace for the small shape
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        out = _decode(x, small)
+    for rep in range(3):
+        with torch.cuda.stream(s):  # larger eager call: the workspace grows
+            bo = _decode(xb, big)
+        s.synchronize()
+        nx = I.decode_inputs(small, seed=60 + rep, device=DEV)
+        for key in ("q", "k_cache", "v_cache", "seqlens"):
+            x[key].copy_(nx[key])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = _decode(nx, small)
+        bref = _decode(xb, big)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep} after growth"
+        assert torch.equal(bo, bref), f"large eager call {rep}"
+    # a fresh stream has no workspace: capturing a split decode there is refused
+    s2 = torch.cuda.Stream()
+    s2.wait_stream(torch.cuda.current_stream())
+    g2 = torch.cuda.CUDAGraph()
+    err = None
+    with torch.cuda.graph(g2, stream=s2):
+        try:
+            _decode(x, small)
+        except gq.GqaError as e:
+            err = e
+    assert err is not None and err.status == gq.GQA_ERR_INVALID_ARG and "captur" in str(err)
+    torch.cuda.synchronize()
