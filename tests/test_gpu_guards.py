@@ -202,6 +202,6 @@ def test_decode_permutation_invariance(H, G):
     ref = O.decode(to_host(x["q"]), to_host(x["k_cache"]), to_host(x["v_cache"]), to_host(x["seqlens"]), w.scale)
     assert_parity(base, ref, w.dtype, "unpermuted")
     assert_parity(perm_out, ref, w.dtype, "permuted")
-    # two bf16 roundings of nearly equal fp32 values differ by at most one ulp
-    diff = (perm_out.float() - base.float()).abs()
-    assert bool((diff <= 2.0 ** -7 * base.float().abs() + 1e-3).all())
+    # the order changes which running maximum each probability is rounded
+    # against, so the two agree to the rounding bar, not bit for bit
+    assert_parity(perm_out, to_host(base).double().numpy(), w.dtype, "permuted against unpermuted")
