@@ -54,13 +54,15 @@ def load_library():
     lib.gqa_decode.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp]
     lib.gqa_decode_ex.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, i32]
     lib.gqa_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, i32, vp, vp]
+    lib.gqa_decode_step_noalloc.argtypes = list(lib.gqa_decode_step.argtypes)
     lib.gqa_prefill.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.gqa_prefill_ex.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.gqa_mean_pool_kv.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp]
     lib.gqa_weighted_pool_kv.argtypes = [vp, vp, i64, i32, i32, i32, i32, vp, vp]
     lib.gqa_decode_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32),
                                     ctypes.POINTER(i32), ctypes.POINTER(i64)]
-    for fn in ("gqa_decode", "gqa_decode_ex", "gqa_decode_step", "gqa_prefill", "gqa_prefill_ex",
+    for fn in ("gqa_decode", "gqa_decode_ex", "gqa_decode_step", "gqa_decode_step_noalloc", "gqa_prefill",
+               "gqa_prefill_ex",
                "gqa_mean_pool_kv", "gqa_weighted_pool_kv", "gqa_decode_plan"):
         getattr(lib, fn).restype = i32
     lib.gqa_status_string.argtypes = [i32]

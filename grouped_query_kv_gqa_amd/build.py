@@ -28,7 +28,8 @@ COMMON = ["-O3", "-std=c++20", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]
 
-SOURCES = ["decode.hip", "prefill.hip", "mean_pool.hip", "gqa_api.cpp", "plan.cpp", "workspace.cpp"]
+SOURCES = ["decode.hip", "decode_noalloc.hip", "prefill.hip", "mean_pool.hip", "gqa_api.cpp", "plan.cpp",
+           "workspace.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -13,6 +13,7 @@
 
 #include "gqa.h"
 #include "kernels.h"
+#include "api_internal.h"
 #include "plan.h"
 #include "workspace.h"
 
@@ -181,6 +182,26 @@ gqa_status decode_impl(const void *q, const void *k_new, const void *v_new, cons
 }
 
 }  // namespace
+
+namespace gqa {
+
+gqa_status set_last_error(gqa_status s, const std::string &msg)
+{
+    return record(s, msg);
+}
+
+gqa_status decode_step_in_workspace(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                                    void *v_cache, const int32_t *seqlens, int B, int H, int G, int d_h, int Tmax,
+                                    float scale, int window, int split_tokens, gqa_dtype dtype, void *out,
+                                    hipStream_t stream, char *ws, int64_t ws_bytes)
+{
+    if (!ws)
+        return record(GQA_ERR_INVALID_ARG, "no workspace");
+    return decode_impl(q, k_new, v_new, k_cache, v_cache, seqlens, B, H, G, d_h, Tmax, scale, window, split_tokens,
+                       dtype, out, stream, static_cast<char *>(ws), ws_bytes);
+}
+
+}  // namespace gqa
 
 extern "C" {
 

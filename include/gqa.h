@@ -97,7 +97,8 @@ typedef enum gqa_dtype { GQA_BF16 = 0, GQA_FP32 = 1, GQA_FP16 = 2 } gqa_dtype;
  * eager call replaces it (it is kept until gqa_release_workspaces), so the
  * graph stays valid. The graph shares the block with every other call on
  * its capture stream: replaying it while such a call (or another graph
- * captured on that stream) runs on a different stream races.
+ * captured on that stream) runs on a different stream races. Callers that
+ * cannot allocate at all use gqa_decode_step_noalloc instead.
  * Requires 1 <= G, G divides H, Tmax >= 0, d_h in {64, 128}; B <= 65535 and
  * B * Tmax < 2^31 (else GQA_ERR_UNSUPPORTED).
  */
@@ -147,6 +148,25 @@ gqa_status gqa_decode_ex(const void *q, const void *k_cache, const void *v_cache
 gqa_status gqa_decode_step(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                            const int32_t *seqlens, int B, int H, int G, int d_h, int Tmax, float scale, int window,
                            int split_tokens, gqa_dtype dtype, void *out, hipStream_t stream);
+
+/*
+ * gqa_decode_step_noalloc -- gqa_decode_step for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments, kernels and results as
+ * gqa_decode_step (bit for bit), but the split workspace is a fixed 32 MiB
+ * device array inside the library, one per GPU, held until the process ends:
+ * nothing is allocated or freed. A decode whose workspace would exceed it
+ * ((splits + B) * H * (d_h + 1) * 4 bytes, with the split count from
+ * gqa_decode_plan; about 10 MB for 64 sequences of 64 heads at d_h = 128)
+ * returns GQA_ERR_UNSUPPORTED and queues nothing. Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or concurrent graph replays) race and must be
+ * serialised by the caller. The array needs no clearing between calls.
+ */
+gqa_status gqa_decode_step_noalloc(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                                   void *v_cache, const int32_t *seqlens, int B, int H, int G, int d_h, int Tmax,
+                                   float scale, int window, int split_tokens, gqa_dtype dtype, void *out,
+                                   hipStream_t stream);
 
 /*
  * gqa_prefill -- attention for every position of B sequences of length T.
