@@ -2,7 +2,8 @@
 
 Usage: ``python -m grouped_query_kv_gqa_amd.build`` or ``build()``. Always
 recompiles; objects go to ``grouped_query_kv_gqa_amd/_build/`` and the
-library to ``grouped_query_kv_gqa_amd/libgqa.so``.
+library to ``grouped_query_kv_gqa_amd/libgqa.so``; the benchmark's bandwidth
+probe goes to ``grouped_query_kv_gqa_amd/libgqa_probe.so``.
 """
 from __future__ import annotations
 
@@ -18,6 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgqa.so")
+PROBE_LIB = os.path.join(PKG, "libgqa_probe.so")  # bandwidth probe for the benchmark only
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -57,7 +59,22 @@ def build(verbose: bool = False) -> str:
     shutil.move(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_probe(verbose)
     return LIB
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The benchmark's HBM bandwidth probe, a separate small library."""
+    os.makedirs(BUILD, exist_ok=True)
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *COMMON, *DEVICE, "-shared", os.path.join(CSRC, "hbm_probe.hip"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for hbm_probe.hip:\n{r.stdout}\n{r.stderr}")
+    shutil.move(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}")
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

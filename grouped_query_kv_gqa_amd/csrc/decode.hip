@@ -109,21 +109,31 @@ __device__ __forceinline__ Span seq_span(int32_t s, int Tmax, int append, int wi
 }
 
 // Flat-position partition shared by the decode and merge kernels (both must
-// compute identical values): total positions and the piece length P. The
-// host guarantees B * Tmax < 2^31, so position counts fit in 32 bits.
-// `n_first` is this lane's span length among the first 64 sequences (0 past
-// B); the caller has read those lengths already and keeps them for its walk.
+// compute identical values): total positions and the piece length P. Every
+// non-empty sequence is preceded by `startup` virtual positions, the cost of
+// starting a piece (first round trips, the combine at its end) in units of
+// positions: a workgroup whose range holds the start of a sequence then takes
+// that many fewer real positions, which evens out the workgroups' finishing
+// times. The host guarantees B * Tmax < 2^31 and bounds startup, so position
+// counts fit in 32 bits. `n_first` is this lane's span length among the
+// first 64 sequences (0 past B); the caller has read those lengths already
+// and keeps them for its walk.
 struct Partition {
     int64_t total;
     int64_t P;
 };
 
-__device__ __forceinline__ Partition make_partition(int n_first, const int32_t *seqlens, int B, int Tmax, int append,
-                                                    int window, int nwg, int fixed_P, int lane)
+__device__ __forceinline__ int with_startup(int n, int startup)
 {
-    int part = n_first;
+    return n > 0 ? n + startup : 0;
+}
+
+__device__ __forceinline__ Partition make_partition(int n_first, const int32_t *seqlens, int B, int Tmax, int append,
+                                                    int window, int nwg, int fixed_P, int startup, int lane)
+{
+    int part = with_startup(n_first, startup);
     for (int i = lane + 64; i < B; i += 64)
-        part += seq_span(seqlens[i], Tmax, append, window).n;
+        part += with_startup(seq_span(seqlens[i], Tmax, append, window).n, startup);
     const int64_t tot = wave_total(part);
     int64_t P;
     if (fixed_P > 0) {
@@ -135,6 +145,16 @@ __device__ __forceinline__ Partition make_partition(int n_first, const int32_t *
             P = kTile;
     }
     return {tot, P};
+}
+
+// Lanes (sequences of a 64-sequence chunk starting at flat position `pre`,
+// inclusive scan `incl` of their lengths with startup positions, real length
+// L) whose real positions meet [lo, hi), as a wave-uniform bit mask. The
+// set bits form one contiguous run.
+__device__ __forceinline__ uint64_t overlapping(int64_t pre, int incl, int L, int64_t lo, int64_t hi)
+{
+    const int64_t first = pre + incl - L;  // first real position of the lane's sequence
+    return __ballot(L > 0 && first < hi && first + L > lo);
 }
 
 // One wave's work on one piece: positions [ta, tb) of sequence b for the
@@ -436,7 +456,7 @@ template <typename T, int D, int NT, int WAVES, int GB, bool APPEND>
 __global__ void __launch_bounds__(WAVES * 64)
 decode_split_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const __bf16 *__restrict__ knew,
                    const __bf16 *__restrict__ vnew, const int32_t *__restrict__ seqlens, int B, int H, int G,
-                   int Tmax, int window, int r, int head_tiles, float scale_log2, int nwg, int fixed_P,
+                   int Tmax, int window, int r, int head_tiles, float scale_log2, int nwg, int fixed_P, int startup,
                    __bf16 *__restrict__ out, float *__restrict__ part, float *__restrict__ lse)
 {
     constexpr int WPG = WAVES / GB;
@@ -456,7 +476,7 @@ decode_split_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const 
     Span sp0 = {0, 0, false};
     if (lane < B)
         sp0 = seq_span(seqlens[lane], Tmax, APPEND, window);
-    const Partition pt = make_partition(sp0.n, seqlens, B, Tmax, APPEND, window, nwg, fixed_P, lane);
+    const Partition pt = make_partition(sp0.n, seqlens, B, Tmax, APPEND, window, nwg, fixed_P, startup, lane);
     const int64_t lo = (int64_t)k * pt.P;
     if (lo >= pt.total)
         return;
@@ -472,20 +492,21 @@ decode_split_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const 
                 sp = seq_span(seqlens[b0 + lane], Tmax, APPEND, window);
         }
         const int Lc = sp.n;
-        const int incl = wave_incl_scan(Lc);
+        const int incl = wave_incl_scan(with_startup(Lc, startup));
         const int64_t chunk_total = __builtin_amdgcn_readlane(incl, 63);
         if (pre + chunk_total <= lo) {
             pre += chunk_total;
             continue;
         }
-        const int n = min(64, B - b0);
-        for (int i = 0; i < n; ++i) {
-            const int L = __builtin_amdgcn_readlane(Lc, i);  // i is wave-uniform
+        // The sequences of this chunk with positions in [lo, hi): one ballot,
+        // then only those (a contiguous run of lanes), in order.
+        uint64_t mine = overlapping(pre, incl, Lc, lo, hi);
+        while (mine) {
+            const int i = __builtin_ctzll(mine);  // wave-uniform
+            mine &= mine - 1;
+            const int L = __builtin_amdgcn_readlane(Lc, i);
+            // first real position of sequence b0 + i in the flat space
             const int64_t pre_b = pre + __builtin_amdgcn_readlane(incl, i) - L;
-            if (pre_b >= hi)
-                return;
-            if (L == 0 || pre_b + L <= lo)
-                continue;
             const int b = b0 + i;
             const int ta = (int)max<int64_t>(lo - pre_b, 0);
             const int tb = (int)min<int64_t>(hi - pre_b, L);
@@ -505,6 +526,419 @@ decode_split_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const 
                                              vnew + new_off, ht == 0, whole, H, G, Tmax, sub, scale_log2,
                                              &vlds[0][0], out, part + slot * D, lse + slot, lane);
         }
+        if (pre + chunk_total >= hi)
+            return;
+        pre += chunk_total;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Wide groups: 33 to 64 query heads per key/value head (multi-query attention
+// at 64 heads is the common case). The narrow kernel above gives such a group
+// several workgroups that each pull the same rows through their compute unit.
+// Here one 8-wave workgroup per (slice, group) streams the group's K/V rows
+// into LDS once, with direct-to-LDS loads, and every wave reads them there:
+//  * waves form 4 head tiles (16 heads each) x 2 position phases; a step
+//    covers 64 positions, 32 per phase;
+//  * the stages (K and V of one step, 32 KiB at d_h = 128) form a ring of
+//    four buffers, and the loads run three steps ahead, so about 96 KiB per
+//    compute unit are in flight while a step is computed; one barrier per
+//    step publishes the stage and frees the buffer the next load reuses;
+//    every row is read once, with the nontemporal cache policy;
+//  * the rows of a stage are swizzled by 16-byte chunk so that the score
+//    fragment reads (16 rows at one chunk, 16-byte reads) and the
+//    transposing V reads (8 rows x 32 bytes per half-wave) spread over all
+//    LDS banks; the buffer range of each stage ends at the piece's last
+//    position, so rows past it arrive as zeros;
+//  * at the end of a piece the second phase of each head tile hands its
+//    softmax state to the first through LDS, which writes the finished rows
+//    or one partial row per head.
+
+// LDS chunk swizzles of a stage row r (16-byte chunk c sits at slot c ^ f(r)).
+template <int D>
+struct WideSwz {
+    // K: the 16 rows a score fragment read takes at one chunk go to 16
+    // different slots (d_h = 128: 16 chunks per row; d_h = 64: 8 chunks, rows
+    // of one parity share a bank half).
+    static __device__ __forceinline__ int k(int r) { return D >= 128 ? (r & 15) : ((r >> 1) & 7); }
+    // V: chunk pairs move together (a transposing read takes 8 bytes of a
+    // 32-byte pair); the 8 rows of a half-wave's read go to 8 different pairs.
+    static __device__ __forceinline__ int v(int r) { return D >= 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
+};
+
+constexpr int kWideWaves = 8;
+constexpr int kWideHeadTiles = 4;                         // 16-head tiles per workgroup
+constexpr int kWidePhases = kWideWaves / kWideHeadTiles;  // position phases
+constexpr int kWideRows = kWidePhases * kTile;            // positions per step
+constexpr int kWideRing = 4;                              // stage buffers; loads run kWideRing - 1 steps ahead
+constexpr float kWideLazy = 8.f;                          // log2 headroom before the softmax reference moves
+
+// s_waitcnt with vmcnt(n) (n < 64), expcnt and lgkmcnt left free.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for data exchanged through LDS only: this wave's LDS
+// operations complete (lgkmcnt(0)), then s_barrier. Unlike __syncthreads()
+// it carries no release fence for global memory, which would wait for every
+// outstanding vector load (vmcnt(0)), including the direct-to-LDS loads of
+// the stages still in flight; the caller waits for the stages it needs.
+__device__ __forceinline__ void lds_barrier()
+{
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt free
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+}
+
+template <typename T, int D, bool APPEND>
+__global__ void __launch_bounds__(kWideWaves * 64)
+decode_wide_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const __bf16 *__restrict__ knew,
+                   const __bf16 *__restrict__ vnew, const int32_t *__restrict__ seqlens, int B, int H, int G,
+                   int Tmax, int window, int r, float scale_log2, int nwg, int fixed_P, int startup,
+                   __bf16 *__restrict__ out,
+                   float *__restrict__ part, float *__restrict__ lse)
+{
+    constexpr int KS = D / 32, DT = D / 16, CH = D / 8;
+    constexpr int RPI = 64 / CH;                        // stage rows one load instruction fills
+    constexpr int NI = kWideRows / (RPI * kWideWaves);  // load instructions per wave per tensor
+    static_assert(NI >= 1 && kWideRows % (RPI * kWideWaves) == 0, "stage rows split evenly over the waves");
+    constexpr int TILE = kWideRows * D;  // elements of one stage tensor
+    using SW = WideSwz<D>;
+    // Separate arrays: the compiler then knows the loads into one buffer do
+    // not touch the buffer being read.
+    __shared__ __attribute__((aligned(256))) __bf16 K0[TILE];
+    __shared__ __attribute__((aligned(256))) __bf16 K1[TILE];
+    __shared__ __attribute__((aligned(256))) __bf16 K2[TILE];
+    __shared__ __attribute__((aligned(256))) __bf16 K3[TILE];
+    __shared__ __attribute__((aligned(256))) __bf16 V0[TILE];
+    __shared__ __attribute__((aligned(256))) __bf16 V1[TILE];
+    __shared__ __attribute__((aligned(256))) __bf16 V2[TILE];
+    __shared__ __attribute__((aligned(256))) __bf16 V3[TILE];
+    auto kbuf = [&](auto i) -> __bf16 * {
+        constexpr int n = decltype(i)::value;
+        if constexpr (n == 0)
+            return K0;
+        else if constexpr (n == 1)
+            return K1;
+        else if constexpr (n == 2)
+            return K2;
+        else
+            return K3;
+    };
+    auto vbuf = [&](auto i) -> __bf16 * {
+        constexpr int n = decltype(i)::value;
+        if constexpr (n == 0)
+            return V0;
+        else if constexpr (n == 1)
+            return V1;
+        else if constexpr (n == 2)
+            return V2;
+        else
+            return V3;
+    };
+
+    const int k = blockIdx.x;
+    const int g = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int ht = wave % kWideHeadTiles, ph = wave / kWideHeadTiles;
+    const int col = lane & 15, kb = lane >> 4;
+    const int h0 = g * r + ht * 16;
+    const int nheads = min(16, r - ht * 16);  // <= 0: a tile past the group (r <= 48)
+    const int64_t tok = (int64_t)G * D;      // elements per cache position
+    const int tok_bytes = G * D * 2;
+    // Per-lane load offsets: instruction u of wave w fills stage rows
+    // (u * waves + w) * RPI + lane / CH, slot lane % CH, so it fetches the
+    // global chunk the swizzle puts in that slot; the swizzle of those rows
+    // does not depend on u.
+    const int drow = wave * RPI + lane / CH;
+    const int dslot = lane % CH;
+    const int voff_k = drow * tok_bytes + g * D * 2 + ((dslot ^ SW::k(drow)) * 16);
+    const int voff_v = drow * tok_bytes + g * D * 2 + ((dslot ^ SW::v(drow)) * 16);
+    const int ustep = kWideWaves * RPI * tok_bytes;
+
+    // LDS element indices of this lane's fragment reads, the same in every
+    // stage: K (A operand of S^T = K q^T) at row 32*ph + 16*mt + col, chunk
+    // 4*s + kb; V^T (A operand of O^T = V^T P^T) at rows 32*ph + 4*kb +
+    // col/4 and 16 rows on, 4 values from column 16*dt + 4*(col%4). Each read
+    // is addressed as stage array + index, with the index opaque to the
+    // compiler: it then still knows which LDS array a read touches (through a
+    // longer chain of pointer arithmetic it loses track and waits for every
+    // load in flight into any stage before the read).
+    int kidx[2][KS], vidx[DT][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const int rr = mt * 16 + col;
+            kidx[mt][s] = (ph * kTile + rr) * D + (((s * 4 + kb) ^ SW::k(rr)) * 8);
+            asm("" : "+v"(kidx[mt][s]));
+        }
+    {
+        const int vr = kb * 4 + (col >> 2);
+        const int vc0 = (col & 3) >> 1, vhalf = (col & 1) * 4;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            vidx[dt][0] = (ph * kTile + vr) * D + (((2 * dt + vc0) ^ SW::v(vr)) * 8) + vhalf;
+            vidx[dt][1] = vidx[dt][0] + 16 * D;
+            asm("" : "+v"(vidx[dt][0]), "+v"(vidx[dt][1]));
+        }
+    }
+
+    Span sp0 = {0, 0, false};
+    if (lane < B)
+        sp0 = seq_span(seqlens[lane], Tmax, APPEND, window);
+    const Partition pt = make_partition(sp0.n, seqlens, B, Tmax, APPEND, window, nwg, fixed_P, startup, lane);
+    const int64_t lo = (int64_t)k * pt.P;
+    if (lo >= pt.total)
+        return;  // the whole workgroup: lo is uniform
+    const int64_t hi = min(lo + pt.P, pt.total);
+
+    int64_t pre = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+        Span sp = sp0;
+        if (b0 > 0) {
+            sp = {0, 0, false};
+            if (b0 + lane < B)
+                sp = seq_span(seqlens[b0 + lane], Tmax, APPEND, window);
+        }
+        const int Lc = sp.n;
+        const int incl = wave_incl_scan(with_startup(Lc, startup));
+        const int64_t chunk_total = __builtin_amdgcn_readlane(incl, 63);
+        if (pre + chunk_total <= lo) {
+            pre += chunk_total;
+            continue;
+        }
+        // The sequences of this chunk with positions in [lo, hi): one ballot,
+        // then only those (a contiguous run of lanes), in order.
+        uint64_t mine = overlapping(pre, incl, Lc, lo, hi);
+        while (mine) {
+            const int i = __builtin_ctzll(mine);  // wave-uniform
+            mine &= mine - 1;
+            const int L = __builtin_amdgcn_readlane(Lc, i);
+            // first real position of sequence b0 + i in the flat space
+            const int64_t pre_b = pre + __builtin_amdgcn_readlane(incl, i) - L;
+            const int b = b0 + i;
+            const int ta = (int)max<int64_t>(lo - pre_b, 0);
+            const int tb = (int)min<int64_t>(hi - pre_b, L);
+            const bool whole = ta == 0 && tb == L;
+            const int64_t slot = ((int64_t)k + b) * H + h0;
+            const int t_off = __builtin_amdgcn_readlane(sp.lo, i);
+            // only the piece that ends at the span end holds the appended token
+            const int t_new = (APPEND && __builtin_amdgcn_readlane((int)sp.appended, i) && tb == L) ? L - 1 : -1;
+            const __bf16 *knew_row = knew + ((int64_t)b * G + g) * D;
+            const __bf16 *vnew_row = vnew + ((int64_t)b * G + g) * D;
+            const __bf16 *kseq = kc + ((int64_t)b * Tmax + t_off) * tok;  // span position 0, every group
+            const __bf16 *vseq = vc + ((int64_t)b * Tmax + t_off) * tok;
+            const int64_t row0 = (int64_t)b * H + h0;
+
+            // q as the MFMA B operand: column = head, k = d chunk (4*s + kb).
+            bf16x8_t qf[KS];
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                u32x4_t v = {0, 0, 0, 0};
+                if (col < nheads)
+                    v = *reinterpret_cast<const u32x4_t *>(q + (row0 + col) * D + (s * 4 + kb) * 8);
+                qf[s] = __builtin_bit_cast(bf16x8_t, v);
+            }
+            float m_run = -INFINITY, l_run = 0.f;
+            f32x4_t acc[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                acc[dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+            const int nsteps = (tb - ta + kWideRows - 1) / kWideRows;
+            // Stage j (positions ta + 64 j ...) into buffer j % kWideRing:
+            // every wave issues its share of the direct-to-LDS loads; rows at
+            // or past tb read as zeros.
+            auto load_stage = [&](auto B_, int j) {
+                const int t0 = ta + j * kWideRows;
+                const int nrec = min(kWideRows, tb - t0) * tok_bytes;
+                buffer_rows_to_lds<NI, kCpolNT>(kseq + (int64_t)t0 * tok, nrec, kbuf(B_) + wave * 512,
+                                                kWideWaves * 512, voff_k, ustep);
+                buffer_rows_to_lds<NI, kCpolNT>(vseq + (int64_t)t0 * tok, nrec, vbuf(B_) + wave * 512,
+                                                kWideWaves * 512, voff_v, ustep);
+            };
+            // This wave's 32 rows of stage j: positions t0 + 32*ph + [0, 32).
+            auto compute = [&](const __bf16 *Kc, const __bf16 *Vc, int j) __attribute__((always_inline)) {
+                const int tc = ta + j * kWideRows + ph * kTile;
+                if (tc >= tb || nheads <= 0)
+                    return;  // wave-uniform
+                f32x4_t st[2];
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    st[mt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) {
+                        const bf16x8_t kf =
+                            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(Kc + kidx[mt][s]));
+                        st[mt] = mfma16x16x32<T>(kf, qf[s], st[mt]);
+                    }
+                }
+                // Online softmax in base 2; lane holds positions tc + 16*mt +
+                // 4*kb + i of head col. Only a tile that crosses the piece end
+                // is masked. The reference m_run moves lazily, only when a
+                // head's maximum exceeds it by more than 2^kLazy, so most
+                // steps skip rescaling the accumulators; probabilities stay
+                // below 2^kLazy (exact in real arithmetic).
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+                    st[mt] *= scale_log2;
+                if (tc + kTile > tb) {
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (tc + mt * 16 + kb * 4 + i >= tb)
+                                st[mt][i] = -INFINITY;
+                }
+                float mx = fmaxf(fmaxf(fmaxf(st[0][0], st[0][1]), fmaxf(st[0][2], st[0][3])),
+                                 fmaxf(fmaxf(st[1][0], st[1][1]), fmaxf(st[1][2], st[1][3])));
+                mx = xor_fmax<16>(mx);
+                mx = xor_fmax<32>(mx);
+                const bool move = mx > m_run + kWideLazy;  // m_run = -inf: the first tile moves it
+                if (__any(move)) {
+                    const float m_new = move ? mx : m_run;
+                    const float alpha = fast_exp2(m_run - m_new);
+                    m_run = m_new;
+                    l_run *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt)
+                        acc[dt] *= alpha;
+                }
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        st[mt][i] = fast_exp2(st[mt][i] - m_run);
+                const bf16x8_t pf = pack8<T>(st[0], st[1]);
+                const u32x4_t pu = __builtin_bit_cast(u32x4_t, pf);
+                float psum = l_run;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    psum = add_pair<T>(pu[jj], psum);
+                l_run = psum;
+                // O^T += V^T P^T, V^T fragments by transposing reads
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const bf16x4_t vlo = lds_read_tr16(Vc + vidx[dt][0]);
+                    const bf16x4_t vhi = lds_read_tr16(Vc + vidx[dt][1]);
+                    const bf16x8_t vf = __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    acc[dt] = mfma16x16x32<T>(vf, pf, acc[dt]);
+                }
+            };
+            // Step j on buffer B_ = j % kWideRing: wait for this wave's loads
+            // of stage j (the loads of the up to two later stages stay in
+            // flight), put the appended token's row in place, publish the
+            // stage with the barrier (which also frees buffer (j - 1) % ring,
+            // read by step j - 1), refill that buffer with stage j + 3, and
+            // compute.
+            auto step = [&](auto B_, int j) __attribute__((always_inline)) {
+                constexpr int b_ = decltype(B_)::value;
+                const int ahead = min(kWideRing - 2, nsteps - 1 - j);  // stages issued after stage j
+                if (ahead >= 2)
+                    wait_vmcnt<4 * NI>();
+                else if (ahead == 1)
+                    wait_vmcnt<2 * NI>();
+                else
+                    wait_vmcnt<0>();
+                if constexpr (APPEND) {
+                    // The wave whose load instruction filled the appended
+                    // token's stage row replaces it with k_new / v_new.
+                    const int rn = t_new - (ta + j * kWideRows);
+                    if (t_new >= 0 && rn >= 0 && rn < kWideRows && (rn / RPI) % kWideWaves == wave && lane < CH) {
+                        const u32x4_t kx = *reinterpret_cast<const u32x4_t *>(knew_row + lane * 8);
+                        const u32x4_t vx = *reinterpret_cast<const u32x4_t *>(vnew_row + lane * 8);
+                        *reinterpret_cast<u32x4_t *>(kbuf(B_) + rn * D + ((lane ^ SW::k(rn)) * 8)) = kx;
+                        *reinterpret_cast<u32x4_t *>(vbuf(B_) + rn * D + ((lane ^ SW::v(rn)) * 8)) = vx;
+                    }
+                }
+                lds_barrier();
+                if (j + kWideRing - 1 < nsteps)
+                    load_stage(Ic<(b_ + kWideRing - 1) % kWideRing>{}, j + kWideRing - 1);
+                compute(kbuf(B_), vbuf(B_), j);
+            };
+
+            load_stage(Ic<0>{}, 0);
+            if (nsteps > 1)
+                load_stage(Ic<1>{}, 1);
+            if (nsteps > 2)
+                load_stage(Ic<2>{}, 2);
+            for (int j = 0;; j += kWideRing) {
+                step(Ic<0>{}, j);
+                if (j + 1 >= nsteps)
+                    break;
+                step(Ic<1>{}, j + 1);
+                if (j + 2 >= nsteps)
+                    break;
+                step(Ic<2>{}, j + 2);
+                if (j + 3 >= nsteps)
+                    break;
+                step(Ic<3>{}, j + 3);
+                if (j + 4 >= nsteps)
+                    break;
+            }
+
+            // The appended token goes from k_new / v_new to the cache; no
+            // workgroup reads that cache row in this call.
+            if constexpr (APPEND) {
+                if (t_new >= 0 && wave == 0 && lane < CH) {
+                    const u32x4_t kx = *reinterpret_cast<const u32x4_t *>(knew_row + lane * 8);
+                    const u32x4_t vx = *reinterpret_cast<const u32x4_t *>(vnew_row + lane * 8);
+                    *reinterpret_cast<u32x4_t *>(kc + ((int64_t)b * Tmax + t_off + t_new) * tok + g * D + lane * 8) =
+                        kx;
+                    *reinterpret_cast<u32x4_t *>(vc + ((int64_t)b * Tmax + t_off + t_new) * tok + g * D + lane * 8) =
+                        vx;
+                }
+            }
+
+            // The second phase of each head tile hands its state to the first
+            // through LDS (stage buffers, free once every wave has left the
+            // loop): accumulators into K0 / K1, maxima and sums into V0.
+            l_run = xor_add<16>(l_run);
+            l_run = xor_add<32>(l_run);
+            static_assert(2 * DT * 256 * 4 <= TILE * 2, "two waves' accumulators fit in one K stage");
+            float *accs = reinterpret_cast<float *>((ht >> 1) ? K1 : K0) + (ht & 1) * DT * 256;
+            float *stat = reinterpret_cast<float *>(V0) + ht * 32;
+            __syncthreads();  // every wave is done with the stages
+            if (ph == 1) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    *reinterpret_cast<f32x4_t *>(accs + dt * 256 + lane * 4) = acc[dt];
+                if (kb == 0) {
+                    stat[col] = m_run;
+                    stat[16 + col] = l_run;
+                }
+            }
+            __syncthreads();
+            if (ph == 0 && col < nheads) {
+                const float m1 = stat[col], l1 = stat[16 + col];
+                const float M = fmaxf(m_run, m1);
+                const float w0 = m_run == -INFINITY ? 0.f : fast_exp2(m_run - M);
+                const float w1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - M);
+                const float Ls = w0 * l_run + w1 * l1;
+                const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const f32x4_t o = w0 * acc[dt] + w1 * *reinterpret_cast<const f32x4_t *>(accs + dt * 256 + lane * 4);
+                    if (whole) {
+                        const f32x4_t x = o * inv;
+                        u32x2_t u = {pack2<T>(x[0], x[1]), pack2<T>(x[2], x[3])};
+                        *reinterpret_cast<u32x2_t *>(out + (row0 + col) * D + kb * 4 + dt * 16) = u;
+                    } else {
+                        *reinterpret_cast<f32x4_t *>(part + (slot + col) * D + kb * 4 + dt * 16) = o * inv;
+                    }
+                }
+                if (!whole && kb == 0)
+                    lse[slot + col] = Ls > 0.f ? M + fast_log2(Ls) : -INFINITY;
+            }
+            __syncthreads();  // the next piece's loads refill the stages
+        }
+        if (pre + chunk_total >= hi)
+            return;
         pre += chunk_total;
     }
 }
@@ -519,7 +953,7 @@ decode_split_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const 
 template <typename T, int D, int NQ>
 __global__ void __launch_bounds__(256)
 decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax, int append, int window, int nwg,
-                    int fixed_P, const float *part, const float *lse, __bf16 *__restrict__ out)
+                    int fixed_P, int startup, const float *part, const float *lse, __bf16 *__restrict__ out)
 {
     constexpr int DCH = 4 * NQ;      // d values per item
     constexpr int NDC = D / DCH;     // items per row
@@ -530,18 +964,19 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
     if (item >= H * NDC)
         return;
 
-    // partition and this sequence's first flat position (each wave on its own)
+    // partition and this sequence's first real flat position, after its
+    // startup positions (each wave on its own)
     int tot_part = 0, pre_part = 0, L_first = 0;
     for (int i = lane; i < B; i += 64) {
         const int Li = seq_span(seqlens[i], Tmax, append, window).n;
-        tot_part += Li;
+        tot_part += with_startup(Li, startup);
         if (i < b)
-            pre_part += Li;
+            pre_part += with_startup(Li, startup);
         if (i == lane)
             L_first = Li;
     }
     const int64_t tot = wave_total(tot_part);
-    const int64_t pre_b = wave_total(pre_part);
+    const int64_t pre_b = wave_total(pre_part) + startup;
     int64_t P;
     if (fixed_P > 0) {
         P = fixed_P;
@@ -630,7 +1065,7 @@ hipError_t launch_merge(const DecodePlan &p, const DecodeArgs &a)
     constexpr int NDC = D / (4 * NQ);
     dim3 grid((unsigned)((a.H * NDC + 3) / 4), (unsigned)a.B);
     decode_merge_kernel<T, D, NQ><<<grid, 256, 0, a.stream>>>(a.seqlens, a.B, a.H, a.Tmax, a.knew != nullptr,
-                                                          a.window, p.nwg, p.fixed_P, a.part, a.lse,
+                                                          a.window, p.nwg, p.fixed_P, p.startup, a.part, a.lse,
                                                           static_cast<__bf16 *>(a.out));
     return hipGetLastError();
 }
@@ -709,6 +1144,29 @@ const void *split_symbol()
     return reinterpret_cast<const void *>(&decode_split_kernel<T, D, NT, WAVES, GB, APPEND>);
 }
 
+// Wide groups: grid (pieces, groups), 8 waves, then the merge.
+template <typename T, int D>
+hipError_t launch_wide(const DecodePlan &p, const DecodeArgs &a)
+{
+    dim3 grid(p.nwg, a.G);
+    __bf16 *kc = const_cast<__bf16 *>(static_cast<const __bf16 *>(a.k));
+    __bf16 *vc = const_cast<__bf16 *>(static_cast<const __bf16 *>(a.v));
+    const __bf16 *q = static_cast<const __bf16 *>(a.q);
+    const __bf16 *kn = static_cast<const __bf16 *>(a.knew), *vn = static_cast<const __bf16 *>(a.vnew);
+    if (a.knew)
+        decode_wide_kernel<T, D, true><<<grid, kWideWaves * 64, 0, a.stream>>>(
+            q, kc, vc, kn, vn, a.seqlens, a.B, a.H, a.G, a.Tmax, a.window, p.r, a.scale * kLog2e, p.nwg, p.fixed_P,
+            p.startup, static_cast<__bf16 *>(a.out), a.part, a.lse);
+    else
+        decode_wide_kernel<T, D, false><<<grid, kWideWaves * 64, 0, a.stream>>>(
+            q, kc, vc, kn, vn, a.seqlens, a.B, a.H, a.G, a.Tmax, a.window, p.r, a.scale * kLog2e, p.nwg, p.fixed_P,
+            p.startup, static_cast<__bf16 *>(a.out), a.part, a.lse);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    return launch_merge_d<T, D>(p, a);
+}
+
 // 16-bit storage of type T; the pointers carry its raw bit patterns.
 template <typename T, int D, int NT, int WAVES, int GB>
 hipError_t launch_split(const DecodePlan &p, const DecodeArgs &a)
@@ -722,11 +1180,11 @@ hipError_t launch_split(const DecodePlan &p, const DecodeArgs &a)
     if (a.knew)
         decode_split_kernel<T, D, NT, WAVES, GB, true><<<grid, WAVES * 64, 0, a.stream>>>(
             q, kc, vc, kn, vn, a.seqlens, a.B, a.H, a.G, a.Tmax, a.window, p.r, p.head_tiles, a.scale * kLog2e,
-            p.nwg, p.fixed_P, static_cast<__bf16 *>(a.out), a.part, a.lse);
+            p.nwg, p.fixed_P, p.startup, static_cast<__bf16 *>(a.out), a.part, a.lse);
     else
         decode_split_kernel<T, D, NT, WAVES, GB, false><<<grid, WAVES * 64, 0, a.stream>>>(
             q, kc, vc, kn, vn, a.seqlens, a.B, a.H, a.G, a.Tmax, a.window, p.r, p.head_tiles, a.scale * kLog2e,
-            p.nwg, p.fixed_P, static_cast<__bf16 *>(a.out), a.part, a.lse);
+            p.nwg, p.fixed_P, p.startup, static_cast<__bf16 *>(a.out), a.part, a.lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -754,6 +1212,21 @@ hipError_t with_variant(const DecodePlan &p, int D, F &&f)
 
 hipError_t decode_blocks_per_cu(const DecodePlan &p, int D, gqa_dtype dtype, bool append, int *blocks)
 {
+    if (p.wide) {
+        const void *f;
+        const bool h = dtype == GQA_FP16;
+        if (D == 64)
+            f = h ? (append ? (const void *)&decode_wide_kernel<_Float16, 64, true>
+                            : (const void *)&decode_wide_kernel<_Float16, 64, false>)
+                  : (append ? (const void *)&decode_wide_kernel<__bf16, 64, true>
+                            : (const void *)&decode_wide_kernel<__bf16, 64, false>);
+        else
+            f = h ? (append ? (const void *)&decode_wide_kernel<_Float16, 128, true>
+                            : (const void *)&decode_wide_kernel<_Float16, 128, false>)
+                  : (append ? (const void *)&decode_wide_kernel<__bf16, 128, true>
+                            : (const void *)&decode_wide_kernel<__bf16, 128, false>);
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, f, kWideWaves * 64, 0);
+    }
     return with_variant(p, D, [&]<int DD, int NTT, int WW, int GG>() {
         const void *f;
         if (dtype == GQA_FP16)
@@ -781,6 +1254,11 @@ hipError_t launch_decode(const DecodePlan &p, const DecodeArgs &a, gqa_dtype dty
             decode_f32_kernel<128><<<grid, 64, 0, a.stream>>>(q, kc, vc, kn, vn, a.seqlens, a.H, a.G, a.Tmax, app,
                                                               a.window, p.r, a.scale, static_cast<float *>(a.out));
         return hipGetLastError();
+    }
+    if (p.wide) {
+        if (dtype == GQA_FP16)
+            return a.D == 64 ? launch_wide<_Float16, 64>(p, a) : launch_wide<_Float16, 128>(p, a);
+        return a.D == 64 ? launch_wide<__bf16, 64>(p, a) : launch_wide<__bf16, 128>(p, a);
     }
     if (dtype == GQA_FP16)
         return with_variant(p, a.D, [&]<int DD, int NTT, int WW, int GG>() {

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #define GQA_LDS __attribute__((address_space(3)))
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -19,6 +21,10 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 namespace gqa {
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// A compile-time integer as a type (selects LDS buffers statically).
+template <int I>
+using Ic = std::integral_constant<int, I>;
 
 // The 16-bit kernels are templates over the storage type T (__bf16 or
 // _Float16). Registers and LDS hold the raw 16-bit patterns in bf16x8_t /
@@ -199,6 +205,29 @@ __device__ __forceinline__ int wave_total(int x)
 __device__ __forceinline__ int clamp_len(int32_t L, int Tmax)
 {
     return L < 0 ? 0 : (L > Tmax ? Tmax : (int)L);
+}
+
+// N buffer_load_dwordx4 ... lds from a raw buffer of nrec bytes at base:
+// instruction u reads byte voff + u*step of the buffer (zeros past nrec) into
+// LDS at dst + u*dst_step elements, lane i at +16*i bytes. The whole byte
+// offset goes in the per-lane (vector) offset: for a raw buffer the range
+// check compares only the vector plus instruction offset with nrec, and a
+// part carried in the scalar offset would be added after the check, so rows
+// past the end would be read instead of returning zeros.
+// CPOL selects the cache policy (0: default; kCpolNT: nontemporal, for rows
+// read once).
+constexpr int kCpolNT = 2;
+
+template <int N, int CPOL = 0>
+__device__ __forceinline__ void buffer_rows_to_lds(const __bf16 *base, int nrec, __bf16 *dst, int dst_step, int voff,
+                                                   int step)
+{
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16 *>(base), (short)0, nrec, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GQA_LDS void *)(dst + u * dst_step), 16, voff + u * step, 0,
+                                                 0, CPOL);
 }
 
 // Wait until every vector memory operation this wave issued has completed

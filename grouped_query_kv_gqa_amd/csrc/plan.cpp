@@ -2,6 +2,7 @@
 // Pure C++ (no HIP); see plan.h.
 #include "plan.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 
@@ -138,21 +139,29 @@ gqa_status plan_decode(int B, int H, int G, int d_h, int Tmax, gqa_dtype dtype, 
         return fail(err, GQA_ERR_INVALID_ARG, "split_tokens must be >= 0");
     DecodePlan p;
     p.r = H / G;
-    // Groups wider than 16 heads take 32-head tiles (more head tiles run as
-    // more workgroups over the same positions). Measured at r = 64 (the G = 1
-    // batch): four 16-head tiles take 84 us against 54 us; one 64-head tile
-    // per wave (478 registers, half of them AGPRs) is within 1%, so no
-    // separate variant is built for it.
-    p.nt = p.r <= 16 ? 1 : 2;
-    p.head_tiles = (int)ceil_div(p.r, 16 * p.nt);
-    // One 16-head tile per wave leaves room for 8-wave workgroups; wider tiles
-    // need the registers of 4-wave workgroups.
-    p.waves = p.nt == 1 ? 8 : 4;
-    p.gb = 1;
-    for (int c : {8, 4, 2}) {
-        if (c <= p.waves && G % c == 0) {
-            p.gb = c;
-            break;
+    if (p.r > 32 && p.r <= 64) {
+        // Wide groups: one 8-wave workgroup per (slice, group) stages the
+        // group's rows in LDS once for all its heads (2 tiles of 32 heads x
+        // 4 position phases).
+        p.wide = 1;
+        p.nt = 2;
+        p.head_tiles = 1;
+        p.waves = 8;
+        p.gb = 1;
+    } else {
+        // Groups wider than 16 heads take 32-head tiles (more head tiles run
+        // as more workgroups over the same positions). One 16-head tile per
+        // wave leaves room for 8-wave workgroups; wider tiles need the
+        // registers of 4-wave workgroups.
+        p.nt = p.r <= 16 ? 1 : 2;
+        p.head_tiles = (int)ceil_div(p.r, 16 * p.nt);
+        p.waves = p.nt == 1 ? 8 : 4;
+        p.gb = 1;
+        for (int c : {8, 4, 2}) {
+            if (c <= p.waves && G % c == 0) {
+                p.gb = c;
+                break;
+            }
         }
     }
     // Launch limits, checked here so that gqa_decode_plan and gqa_decode
@@ -174,7 +183,19 @@ gqa_status plan_decode(int B, int H, int G, int d_h, int Tmax, gqa_dtype dtype, 
     const int64_t combos = (int64_t)(G / p.gb) * p.head_tiles;
     if (combos > 65535)
         return fail(err, GQA_ERR_UNSUPPORTED, "too many key/value heads");
-    const int64_t positions = (int64_t)B * Tmax;
+    // Startup positions (wide kernel only): the piece startup cost over the
+    // bytes a workgroup streams per position (one group's K and V rows). The
+    // narrow kernel reads 8 groups per position, where a piece's start costs
+    // a few positions only, and there the charge measured slower: it moves
+    // slice boundaries off sequence boundaries in uniform batches, giving
+    // workgroups two pieces each.
+    if (split_tokens == 0 && p.wide) {
+        const int64_t per_pos = (int64_t)p.gb * d_h * 2 * elem_size(dtype);
+        p.startup = (int)std::min<int64_t>(kPieceStartupBytes / per_pos, 4096);
+        if ((int64_t)B * (Tmax + p.startup) > 0x7fffffff)
+            p.startup = 0;  // keep flat positions within 31 bits
+    }
+    const int64_t positions = (int64_t)B * (Tmax + p.startup);
     const int64_t max_pieces = ceil_div(positions > 0 ? positions : 1, kDecodeTile);
     int64_t nwg;
     if (split_tokens > 0) {
@@ -183,7 +204,7 @@ gqa_status plan_decode(int B, int H, int G, int d_h, int Tmax, gqa_dtype dtype, 
         p.full_P = p.fixed_P;
     } else {
         const int64_t cus = cu_count > 0 ? cu_count : 256;
-        const int64_t bpc = blocks_per_cu > 0 ? blocks_per_cu : default_blocks_per_cu(d_h, p.nt);
+        const int64_t bpc = blocks_per_cu > 0 ? blocks_per_cu : (p.wide ? 1 : default_blocks_per_cu(d_h, p.nt));
         nwg = (cus * bpc) / combos;
         if (nwg < 1)
             nwg = 1;

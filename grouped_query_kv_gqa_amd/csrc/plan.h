@@ -12,9 +12,11 @@ namespace gqa {
 
 // Decode launch plan. The cache positions of all sequences, laid end to end,
 // are cut into equal pieces, one per workgroup along grid x; grid y covers
-// (group blocks of gb key/value groups) x (head tiles of 16*nt query heads).
+// (group blocks of gb key/value groups) x (head tiles of 16*nt query heads),
+// or the G groups for the wide kernel.
 struct DecodePlan {
     int r = 0;           // query heads per group, H / G
+    int wide = 0;        // 1: groups of 33..64 heads, one 8-wave workgroup per (slice, group) with LDS stages
     int nt = 1;          // 16-head MFMA column tiles per wave: 1 or 2
     int head_tiles = 1;  // ceil(r / (16 * nt))
     int waves = 8;       // wavefronts per workgroup
@@ -22,6 +24,7 @@ struct DecodePlan {
     int nwg = 1;         // workgroups along the flat position space (grid x)
     int fixed_P = 0;     // piece length when set by the caller, else 0 (balanced on the device)
     int full_P = 32;     // piece length when every sequence has Tmax positions
+    int startup = 0;     // virtual positions before each sequence (the cost of starting a piece); 0 with fixed_P
     int merge_nq = 8;    // merge kernel: d-quads per wave (64/merge_nq lanes share a quad)
     int64_t part_offset = 0;      // fp32 partial rows [nwg + B][H][d_h]
     int64_t lse_offset = 0;       // fp32 base-2 log-sum-exp [nwg + B][H]
@@ -29,6 +32,11 @@ struct DecodePlan {
 };
 
 constexpr int kDecodeTile = 32;  // cache positions per wavefront iteration
+// Bytes a workgroup could have streamed in the time it spends starting a
+// piece (first round trips, then the combine and stores at its end), about
+// 5 us at a compute unit's share of the bandwidth: the balanced partition
+// charges each sequence this many bytes' worth of positions.
+constexpr int64_t kPieceStartupBytes = 128 * 1024;
 
 // Workgroups of a decode variant that fit on one compute unit, as measured
 // for the gfx950 build (used when the runtime is not asked).

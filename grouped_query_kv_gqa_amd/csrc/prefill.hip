@@ -181,27 +181,6 @@ __device__ __forceinline__ u32x4_t ld16(const __bf16 *p)
     return *reinterpret_cast<const u32x4_t *>(p);
 }
 
-template <int I>
-using Ic = std::integral_constant<int, I>;
-
-// N buffer_load_dwordx4 ... lds from a raw buffer of nrec bytes at base:
-// instruction u reads byte voff + u*step of the buffer (zeros past nrec) into
-// LDS at dst + u*dst_step elements, lane i at +16*i bytes. The whole byte
-// offset goes in the per-lane (vector) offset: for a raw buffer the range
-// check compares only the vector plus instruction offset with nrec, and a
-// part carried in the scalar offset would be added after the check, so rows
-// past the end would be read instead of returning zeros.
-template <int N>
-__device__ __forceinline__ void buffer_rows_to_lds(const __bf16 *base, int nrec, __bf16 *dst, int dst_step, int voff,
-                                                   int step)
-{
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16 *>(base), (short)0, nrec, 0x00020000);
-#pragma unroll
-    for (int u = 0; u < N; ++u)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GQA_LDS void *)(dst + u * dst_step), 16, voff + u * step, 0,
-                                                 0, 0);
-}
 
 // Software pipeline over key tiles, one barrier per tile. Iteration j holds
 // the scores S_j of tile j in registers and, in one basic block, computes

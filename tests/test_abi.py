@@ -91,11 +91,15 @@ def test_decode_plan():
     assert (chunk, nwg) == (256, 256)
     slots = (256 + 16) * 32
     assert ws == slots * 128 * 4 + slots * 4
-    # explicit slice lengths round up to 32 positions
+    # explicit slice lengths round up to 32 positions and charge no startup
     assert gq.decode_plan(2, 8, 2, 128, 1000, split_tokens=100)[:2] == (128, 16)
     assert gq.decode_plan(2, 8, 2, 128, 1000, split_tokens=5000)[:2] == (5024, 1)
     # one long sequence spread over every CU
     assert gq.decode_plan(1, 64, 8, 128, 131072)[:2] == (512, 256)
+    # multi-query (one group of 64 heads, the wide kernel): one 8-wave
+    # workgroup per CU reading 512 B per position, charged 128 KiB / 512 B =
+    # 256 startup positions per sequence: 64 x (8192 + 256) / 256 = 2112
+    assert gq.decode_plan(64, 64, 1, 128, 8192)[:2] == (2112, 256)
     # fp32 never splits
     import torch
     assert gq.decode_plan(1, 8, 2, 64, 256, dtype=torch.float32) == (256, 1, 0)
@@ -121,7 +125,8 @@ int main() {
     if (H % G) continue;
     for (int T : {0, 1, 31, 32, 33, 4096, 131072}) for (int s : {0, 32, 100, 1 << 20}) for (int bpc : {0, 1, 2}) {
       assert(gqa::plan_decode(B, H, G, 128, T, GQA_BF16, s, 256, bpc, &p, &e) == GQA_OK);
-      assert(p.head_tiles * 16 * p.nt >= H / G && G % p.gb == 0 && p.waves % p.gb == 0);
+      assert((p.wide ? 64 : p.head_tiles * 16 * p.nt) >= H / G && G % p.gb == 0 && p.waves % p.gb == 0);
+      assert(p.wide == (H / G > 32 && H / G <= 64));
       if (B == 0) continue;
       assert(p.nwg >= 1 && p.full_P >= 32 && p.full_P % 32 == 0);
       assert((int64_t)p.full_P * p.nwg >= (int64_t)B * T);

@@ -265,3 +265,41 @@ def test_decode_shared_group_deterministic(H, G, D):
     ref_a, _, _ = O.decode_step(to_host(x["q"]), to_host(x["k_cache"]), to_host(x["v_cache"]), to_host(x["seqlens"]),
                                 w.scale, k_new=to_host(kn), v_new=to_host(vn))
     assert_parity(outs[0], ref_a, torch.bfloat16, "decode_step append")
+
+
+WIDE = [
+    # B, H, G, D, Tmax, seqlens, dtype: 33 to 64 heads per group (one
+    # workgroup per slice and group, K/V staged in LDS for all heads)
+    (3, 64, 1, 128, 1000, [1000, 129, 1], torch.bfloat16),
+    (2, 33, 1, 128, 700, [700, 300], torch.bfloat16),      # a 1-head second tile
+    (4, 96, 2, 64, 600, [600, 0, 127, 128], torch.bfloat16),
+    (2, 120, 3, 128, 450, [449, 450], torch.float16),      # 40 heads per group
+    (5, 48, 1, 64, 2100, [2100, 1, 2048, 777, 1500], torch.float16),
+]
+
+
+@pytest.mark.parametrize("B,H,G,D,Tmax,seqlens,dtype", WIDE)
+def test_decode_wide_groups(B, H, G, D, Tmax, seqlens, dtype):
+    """Groups of 33 to 64 heads against the oracle, whole and cut into
+    pieces, with an append into the cache and with a window."""
+    say(f"decode wide B={B} H={H} G={G} D={D} Tmax={Tmax} {dtype}")
+    w = I.DecodeWorkload("wide", B, H, G, D, Tmax, dtype)
+    x = I.decode_inputs(w, seed=H * 7 + G + D, device=DEV, seqlens=seqlens)
+    ref = O.decode(to_host(x["q"]), to_host(x["k_cache"]), to_host(x["v_cache"]), to_host(x["seqlens"]), w.scale)
+    for split in (0, 32, 160, 4096):
+        out = _run(x, w.scale, split)
+        assert_parity(out, ref, dtype, f"split={split}")
+    kn = I.random_tensor((B, G, D), seed=31, dtype=dtype, device=DEV)
+    vn = I.random_tensor((B, G, D), seed=32, dtype=dtype, device=DEV)
+    for window, split in ((0, 0), (0, 96), (200, 0), (1, 64)):
+        ref_s, kr, vr = O.decode_step(to_host(x["q"]), to_host(x["k_cache"]), to_host(x["v_cache"]),
+                                      to_host(x["seqlens"]), w.scale, k_new=to_host(kn), v_new=to_host(vn),
+                                      window=window)
+        kc, vc = x["k_cache"].clone(), x["v_cache"].clone()
+        torch.cuda.synchronize()
+        out = gq.decode_step(x["q"], kc, vc, x["seqlens"], scale=w.scale, k_new=kn, v_new=vn, window=window,
+                             split_tokens=split)
+        torch.cuda.synchronize()
+        assert_parity(out, ref_s, dtype, f"append window={window} split={split}")
+        assert np.array_equal(to_host(kc).view(torch.int16).numpy().view(np.uint16), kr)
+        assert np.array_equal(to_host(vc).view(torch.int16).numpy().view(np.uint16), vr)
