@@ -749,6 +749,15 @@ decode_wide_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const _
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
                 acc[dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+            // The appended token's rows, read before the stage loads so that
+            // no other vector load sits between them in the loop.
+            u32x4_t knew_reg = {0, 0, 0, 0}, vnew_reg = {0, 0, 0, 0};
+            if constexpr (APPEND) {
+                if (t_new >= 0 && lane < CH) {
+                    knew_reg = *reinterpret_cast<const u32x4_t *>(knew_row + lane * 8);
+                    vnew_reg = *reinterpret_cast<const u32x4_t *>(vnew_row + lane * 8);
+                }
+            }
 
             const int nsteps = (tb - ta + kWideRows - 1) / kWideRows;
             // Stage j (positions ta + 64 j ...) into buffer j % kWideRing:
@@ -850,10 +859,8 @@ decode_wide_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const _
                     // token's stage row replaces it with k_new / v_new.
                     const int rn = t_new - (ta + j * kWideRows);
                     if (t_new >= 0 && rn >= 0 && rn < kWideRows && (rn / RPI) % kWideWaves == wave && lane < CH) {
-                        const u32x4_t kx = *reinterpret_cast<const u32x4_t *>(knew_row + lane * 8);
-                        const u32x4_t vx = *reinterpret_cast<const u32x4_t *>(vnew_row + lane * 8);
-                        *reinterpret_cast<u32x4_t *>(kbuf(B_) + rn * D + ((lane ^ SW::k(rn)) * 8)) = kx;
-                        *reinterpret_cast<u32x4_t *>(vbuf(B_) + rn * D + ((lane ^ SW::v(rn)) * 8)) = vx;
+                        *reinterpret_cast<u32x4_t *>(kbuf(B_) + rn * D + ((lane ^ SW::k(rn)) * 8)) = knew_reg;
+                        *reinterpret_cast<u32x4_t *>(vbuf(B_) + rn * D + ((lane ^ SW::v(rn)) * 8)) = vnew_reg;
                     }
                 }
                 lds_barrier();
@@ -886,12 +893,10 @@ decode_wide_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const _
             // workgroup reads that cache row in this call.
             if constexpr (APPEND) {
                 if (t_new >= 0 && wave == 0 && lane < CH) {
-                    const u32x4_t kx = *reinterpret_cast<const u32x4_t *>(knew_row + lane * 8);
-                    const u32x4_t vx = *reinterpret_cast<const u32x4_t *>(vnew_row + lane * 8);
                     *reinterpret_cast<u32x4_t *>(kc + ((int64_t)b * Tmax + t_off + t_new) * tok + g * D + lane * 8) =
-                        kx;
+                        knew_reg;
                     *reinterpret_cast<u32x4_t *>(vc + ((int64_t)b * Tmax + t_off + t_new) * tok + g * D + lane * 8) =
-                        vx;
+                        vnew_reg;
                 }
             }
 

@@ -33,10 +33,12 @@ struct DecodePlan {
 
 constexpr int kDecodeTile = 32;  // cache positions per wavefront iteration
 // Bytes a workgroup could have streamed in the time it spends starting a
-// piece (first round trips, then the combine and stores at its end), about
-// 5 us at a compute unit's share of the bandwidth: the balanced partition
-// charges each sequence this many bytes' worth of positions.
-constexpr int64_t kPieceStartupBytes = 128 * 1024;
+// piece (the first stages' round trip, then the combine and stores at its
+// end), about 5-10 us at a compute unit's share of the bandwidth: the
+// balanced partition of the wide kernel charges each sequence this many
+// bytes' worth of positions (measured on the multi-query batch: 64 KiB
+// 39.2 us, 128 KiB 38.8 us, 256 KiB 38.2 us, none 40.0 us).
+constexpr int64_t kPieceStartupBytes = 256 * 1024;
 
 // Workgroups of a decode variant that fit on one compute unit, as measured
 // for the gfx950 build (used when the runtime is not asked).
