@@ -66,7 +66,8 @@ DECODE_CONFIGS = [
 # rocprofv3 FETCH_SIZE / WRITE_SIZE summaries, one per timed workload
 TRAFFIC_PROFILES = {key: f"{key}_hbm_counters.md" for key, _, _ in DECODE_CONFIGS}
 TRAFFIC_PROFILES[PREFILL_WORKLOAD] = "prefill_b4_t8192_hbm_counters.md"
-DECODE_SOURCES = ["grouped_query_kv_gqa_amd/csrc/decode.hip", "grouped_query_kv_gqa_amd/csrc/device_common.h"]
+DECODE_SOURCES = ["grouped_query_kv_gqa_amd/csrc/decode.hip", "grouped_query_kv_gqa_amd/csrc/device_common.h",
+                  "grouped_query_kv_gqa_amd/csrc/plan.h", "grouped_query_kv_gqa_amd/csrc/plan.cpp"]
 PREFILL_SOURCES = ["grouped_query_kv_gqa_amd/csrc/prefill.hip", "grouped_query_kv_gqa_amd/csrc/device_common.h"]
 
 

@@ -36,9 +36,11 @@ constexpr int kDecodeTile = 32;  // cache positions per wavefront iteration
 // piece (the first stages' round trip, then the combine and stores at its
 // end), about 5-10 us at a compute unit's share of the bandwidth: the
 // balanced partition of the wide kernel charges each sequence this many
-// bytes' worth of positions (measured on the multi-query batch: 64 KiB
-// 39.2 us, 128 KiB 38.8 us, 256 KiB 38.2 us, none 40.0 us).
-constexpr int64_t kPieceStartupBytes = 256 * 1024;
+// bytes' worth of positions (measured on the multi-query batch: none
+// 40.0 us, 64 KiB 39.2 us, 128 KiB 38.8 us, 256 KiB 38.2 us; on another GPU
+// 256 KiB 39.1-39.3 us, 384 KiB 38.9 us, 512 KiB 38.8-38.9 us, 768 KiB
+// 39.6-39.7 us, 1 MiB 40.0-40.2 us).
+constexpr int64_t kPieceStartupBytes = 512 * 1024;
 
 // Workgroups of a decode variant that fit on one compute unit, as measured
 // for the gfx950 build (used when the runtime is not asked).

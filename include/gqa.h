@@ -225,7 +225,7 @@ gqa_status gqa_mean_pool_kv(const void *in, int64_t N, int H, int G, int d_h, gq
  * per workgroup when every sequence holds Tmax positions (shorter sequences
  * shrink the slice on the device), and the workspace bytes. For groups of
  * 33 to 64 heads with split_tokens = 0, each sequence is also charged
- * startup positions (256 KiB divided by the K/V bytes a workgroup reads per
+ * startup positions (512 KiB divided by the K/V bytes a workgroup reads per
  * position), the cost of starting a piece, so that workgroups holding the
  * start of a sequence take fewer real positions. For the fp32
  * path: chunk_tokens = Tmax, num_splits = 1, workspace 0. `cu_count` is the

@@ -97,9 +97,9 @@ def test_decode_plan():
     # one long sequence spread over every CU
     assert gq.decode_plan(1, 64, 8, 128, 131072)[:2] == (512, 256)
     # multi-query (one group of 64 heads, the wide kernel): one 8-wave
-    # workgroup per CU reading 512 B per position, charged 256 KiB / 512 B =
-    # 512 startup positions per sequence: 64 x (8192 + 512) / 256 = 2176
-    assert gq.decode_plan(64, 64, 1, 128, 8192)[:2] == (2176, 256)
+    # workgroup per CU reading 512 B per position, charged 512 KiB / 512 B =
+    # 1024 startup positions per sequence: 64 x (8192 + 1024) / 256 = 2304
+    assert gq.decode_plan(64, 64, 1, 128, 8192)[:2] == (2304, 256)
     # fp32 never splits
     import torch
     assert gq.decode_plan(1, 8, 2, 64, 256, dtype=torch.float32) == (256, 1, 0)
