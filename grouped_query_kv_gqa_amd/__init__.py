@@ -11,19 +11,25 @@ raises.
   decode(q, k_cache, v_cache, seqlens, scale=None, out=None, split_tokens=0)
   prefill(q, k, v, causal=True, out=None)
   mean_pool_kv(x, G, out=None)
+
+Inside ``with debug_build():`` the calls go to ``libgqa_debug.so`` instead,
+the same kernels with a range check at every global memory access;
+``debug_checks()`` reads (and clears) the violations they recorded.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
 import torch
 
 __all__ = ["GqaError", "decode", "decode_step", "prefill", "mean_pool_kv", "weighted_pool_kv", "decode_plan",
-           "release_workspaces", "library_path", "load_library"]
+           "release_workspaces", "library_path", "load_library", "debug_build", "debug_checks"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libgqa.so")
+_DEBUG_LIB_PATH = os.path.join(_PKG, "libgqa_debug.so")
 
 GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_HIP = 0, 1, 2, 3
 GQA_BF16, GQA_FP32, GQA_FP16 = 0, 1, 2
@@ -41,15 +47,49 @@ def library_path() -> str:
     return _LIB_PATH
 
 
+_debug_lib = None
+_use_debug = False
+
+
 def load_library():
     """Load libgqa.so (torch is imported first, so the library binds to the
-    HIP runtime torch already loaded)."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is not built; run `python -m grouped_query_kv_gqa_amd.build`")
-    lib = ctypes.CDLL(_LIB_PATH)
+    HIP runtime torch already loaded); libgqa_debug.so inside debug_build()."""
+    global _lib, _debug_lib
+    if _use_debug:
+        if _debug_lib is None:
+            _debug_lib = _open(_DEBUG_LIB_PATH)
+        return _debug_lib
+    if _lib is None:
+        _lib = _open(_LIB_PATH)
+    return _lib
+
+
+@contextlib.contextmanager
+def debug_build():
+    """Route this module's calls to libgqa_debug.so inside the block."""
+    global _use_debug
+    prev = _use_debug
+    _use_debug = True
+    try:
+        yield
+    finally:
+        _use_debug = prev
+
+
+def debug_checks():
+    """(enabled, flags) from gqa_debug_checks of the library in use: enabled
+    is False for the release library; flags (0 = none) are the range-check
+    violations recorded on the current device since the last call."""
+    lib = load_library()
+    en, fl = ctypes.c_int(), ctypes.c_uint32()
+    _check(lib.gqa_debug_checks(ctypes.byref(en), ctypes.byref(fl)))
+    return bool(en.value), fl.value
+
+
+def _open(path: str):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m grouped_query_kv_gqa_amd.build`")
+    lib = ctypes.CDLL(path)
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
     lib.gqa_decode.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp]
     lib.gqa_decode_ex.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, i32]
@@ -75,7 +115,10 @@ def load_library():
     lib.gqa_release_workspaces.restype = i32
     lib.gqa_abi_version.argtypes = []
     lib.gqa_abi_version.restype = i32
-    _lib = lib
+    lib.gqa_debug_checks.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_uint32)]
+    lib.gqa_debug_checks.restype = i32
+    lib.gqa_debug_selftest.argtypes = [vp]
+    lib.gqa_debug_selftest.restype = i32
     return lib
 
 

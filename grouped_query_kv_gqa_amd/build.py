@@ -2,7 +2,9 @@
 
 Usage: ``python -m grouped_query_kv_gqa_amd.build`` or ``build()``. Always
 recompiles; objects go to ``grouped_query_kv_gqa_amd/_build/`` and the
-library to ``grouped_query_kv_gqa_amd/libgqa.so``; the benchmark's bandwidth
+library to ``grouped_query_kv_gqa_amd/libgqa.so``. The same sources built
+with ``-DGQA_DEBUG`` (device range checks on every global access, see
+``gqa_debug_checks``) give ``libgqa_debug.so``; the benchmark's bandwidth
 probe goes to ``grouped_query_kv_gqa_amd/libgqa_probe.so``.
 """
 from __future__ import annotations
@@ -19,6 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgqa.so")
+DEBUG_LIB = os.path.join(PKG, "libgqa_debug.so")  # range-checked build, for tests
 PROBE_LIB = os.path.join(PKG, "libgqa_probe.so")  # bandwidth probe for the benchmark only
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -34,31 +37,39 @@ SOURCES = ["decode.hip", "decode_noalloc.hip", "prefill.hip", "mean_pool.hip", "
            "workspace.cpp"]
 
 
-def _compile(src: str) -> str:
+def _compile(job) -> str:
+    src, debug = job
     path = os.path.join(CSRC, src)
-    obj = os.path.join(BUILD, src + ".o")
+    obj = os.path.join(BUILD, ("debug_" if debug else "") + src + ".o")
+    flags = [*COMMON, "-DGQA_DEBUG"] if debug else COMMON
     if src.endswith(".hip"):
-        cmd = [HIPCC, *COMMON, *DEVICE, "-c", path, "-o", obj]
+        cmd = [HIPCC, *flags, *DEVICE, "-c", path, "-o", obj]
     else:
-        cmd = [HIPCC, *COMMON, "-c", path, "-o", obj]
+        cmd = [HIPCC, *flags, "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    shutil.move(tmp, LIB)
+    shutil.move(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {lib}")
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = [(src, debug) for debug in (False, True) for src in SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        objs = list(ex.map(_compile, jobs))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], DEBUG_LIB, verbose)
     build_probe(verbose)
     return LIB
 

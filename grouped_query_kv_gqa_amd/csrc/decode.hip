@@ -174,7 +174,7 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
                                              const __bf16 *knew_row, const __bf16 *vnew_row, bool store_new,
                                              bool whole, int H, int G, int Tmax, int sub, float scale_log2,
                                              __bf16 *vl_all, __bf16 *__restrict__ out, float *__restrict__ part_row,
-                                             float *__restrict__ lse_row, int lane)
+                                             float *__restrict__ lse_row, int lane, bool store_ok)
 {
     const int wave = threadIdx.x >> 6;
     __bf16 *vl = vl_all + wave * kTile * TileCfg<D, NT>::LDS_STRIDE;  // this wave's V tile
@@ -190,7 +190,7 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) {
             u32x4_t v = {0, 0, 0, 0};
-            if (hh < nheads)
+            if (hh < nheads && GQA_IN_RANGE(h0 + hh, H, 1))
                 v = load16(q + (row0 + hh) * D + (s * 4 + kb) * 8);
             qf[nt][s] = __builtin_bit_cast(bf16x8_t, v);
         }
@@ -223,9 +223,10 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
             const __bf16 *src = kbase + t * tok_stride;
             if constexpr (APPEND)
                 src = (t == t_new) ? knew_row : src;
+            const bool ok = (APPEND && t == t_new) || GQA_IN_RANGE(t_off + t, Tmax, 0);
 #pragma unroll
             for (int s = 0; s < C::KS; ++s)
-                kr[mt][s] = load16_kv<NT == 1>(src + (s * 4 + kb) * 8);
+                kr[mt][s] = ok ? load16_kv<NT == 1>(src + (s * 4 + kb) * 8) : (u32x4_t){0, 0, 0, 0};
         }
     };
     auto load_v = [&](int t0, u32x4_t (&vr)[C::VLOADS]) {
@@ -235,7 +236,8 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
             const __bf16 *src = vbase + t * tok_stride;
             if constexpr (APPEND)
                 src = (t == t_new) ? vnew_row : src;
-            vr[i] = load16_kv<NT == 1>(src + (lane % C::CH) * 8);
+            const bool ok = (APPEND && t == t_new) || GQA_IN_RANGE(t_off + t, Tmax, 0);
+            vr[i] = ok ? load16_kv<NT == 1>(src + (lane % C::CH) * 8) : (u32x4_t){0, 0, 0, 0};
         }
     };
 
@@ -359,7 +361,8 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
     // have been issued leaves the compiler unsure how many memory operations
     // are outstanding, so it would wait for all of them at every tile.
     if constexpr (APPEND) {
-        if (store_new && sub == 0 && t_new >= 0 && lane < C::CH) {
+        if (store_new && sub == 0 && t_new >= 0 && lane < C::CH && store_ok &&
+            GQA_IN_RANGE(t_off + t_new, Tmax, 2)) {
             const u32x4_t kx = load16(knew_row + lane * 8);
             const u32x4_t vx = load16(vnew_row + lane * 8);
             *reinterpret_cast<u32x4_t *>(kbase + t_new * tok_stride + lane * 8) = kx;
@@ -379,7 +382,7 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
     // base-2 log-sum-exp. Lane (col, kb) holds d = dt*16 + 4*kb + i.
     auto emit = [&](int nt, int dt, const f32x4_t &o, float inv) {
         const int hh = nt * 16 + col;
-        if (hh >= nheads)
+        if (hh >= nheads || !store_ok)
             return;
         if (whole) {
             const f32x4_t x = o * inv;
@@ -396,7 +399,7 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt)
                 emit(nt, dt, acc[nt][dt], inv);
-            if (!whole && kb == 0 && nt * 16 + col < nheads)
+            if (!whole && kb == 0 && nt * 16 + col < nheads && store_ok)
                 lse_row[nt * 16 + col] = l_run[nt] > 0.f ? m_run[nt] + fast_log2(l_run[nt]) : -INFINITY;
         }
     } else {
@@ -445,7 +448,7 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
                     o += wj[j] * *reinterpret_cast<const f32x4_t *>(grp + j * REG + dt * 256 + lane * 4);
                 emit(nt, dt, o, inv);
             }
-            if (!whole && sub == 0 && kb == 0 && nt * 16 + col < nheads)
+            if (!whole && sub == 0 && kb == 0 && nt * 16 + col < nheads && store_ok)
                 lse_row[nt * 16 + col] = L > 0.f ? M + fast_log2(L) : -INFINITY;
         }
         __syncthreads();  // the next piece's loop refills the V tiles
@@ -522,9 +525,14 @@ decode_split_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const 
             const int t_new =
                 (APPEND && __builtin_amdgcn_readlane((int)sp.appended, i) && tb == L) ? L - 1 : -1;
             const int64_t new_off = ((int64_t)b * G + g) * D;
+            // (debug builds: the piece's sequence, group, heads and partial
+            // rows; a failure skips its stores, never its barriers)
+            const bool store_ok = GQA_IN_RANGE(b, B, 4) && GQA_IN_RANGE(g, G, 4) &&
+                                  GQA_IN_RANGE(h0 + nheads - 1, H, 4) &&
+                                  (whole || GQA_IN_RANGE(slot + nheads - 1, (int64_t)(nwg + B) * H, 5));
             decode_piece<T, D, NT, WPG, APPEND>(q, kc, vc, b, g, h0, nheads, lo_b, ta, tb, t_new, knew + new_off,
                                              vnew + new_off, ht == 0, whole, H, G, Tmax, sub, scale_log2,
-                                             &vlds[0][0], out, part + slot * D, lse + slot, lane);
+                                             &vlds[0][0], out, part + slot * D, lse + slot, lane, store_ok);
         }
         if (pre + chunk_total >= hi)
             return;
@@ -740,7 +748,7 @@ decode_wide_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const _
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 u32x4_t v = {0, 0, 0, 0};
-                if (col < nheads)
+                if (col < nheads && GQA_IN_RANGE(row0 + col, (int64_t)B * H, 6))
                     v = *reinterpret_cast<const u32x4_t *>(q + (row0 + col) * D + (s * 4 + kb) * 8);
                 qf[s] = __builtin_bit_cast(bf16x8_t, v);
             }
@@ -766,10 +774,12 @@ decode_wide_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const _
             auto load_stage = [&](auto B_, int j) {
                 const int t0 = ta + j * kWideRows;
                 const int nrec = min(kWideRows, tb - t0) * tok_bytes;
-                buffer_rows_to_lds<NI, kCpolNT>(kseq + (int64_t)t0 * tok, nrec, kbuf(B_) + wave * 512,
-                                                kWideWaves * 512, voff_k, ustep);
-                buffer_rows_to_lds<NI, kCpolNT>(vseq + (int64_t)t0 * tok, nrec, vbuf(B_) + wave * 512,
-                                                kWideWaves * 512, voff_v, ustep);
+                if (GQA_IN_RANGE(t_off + t0, Tmax, 7) && GQA_IN_RANGE(t_off + t0 + min(kWideRows, tb - t0) - 1, Tmax, 7)) {
+                    buffer_rows_to_lds<NI, kCpolNT>(kseq + (int64_t)t0 * tok, nrec, kbuf(B_) + wave * 512,
+                                                    kWideWaves * 512, voff_k, ustep);
+                    buffer_rows_to_lds<NI, kCpolNT>(vseq + (int64_t)t0 * tok, nrec, vbuf(B_) + wave * 512,
+                                                    kWideWaves * 512, voff_v, ustep);
+                }
             };
             // This wave's 32 rows of stage j: positions t0 + 32*ph + [0, 32).
             auto compute = [&](const __bf16 *Kc, const __bf16 *Vc, int j) __attribute__((always_inline)) {
@@ -892,7 +902,8 @@ decode_wide_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const _
             // The appended token goes from k_new / v_new to the cache; no
             // workgroup reads that cache row in this call.
             if constexpr (APPEND) {
-                if (t_new >= 0 && wave == 0 && lane < CH) {
+                if (t_new >= 0 && wave == 0 && lane < CH && GQA_IN_RANGE(b, B, 4) &&
+                    GQA_IN_RANGE(t_off + t_new, Tmax, 2)) {
                     *reinterpret_cast<u32x4_t *>(kc + ((int64_t)b * Tmax + t_off + t_new) * tok + g * D + lane * 8) =
                         knew_reg;
                     *reinterpret_cast<u32x4_t *>(vc + ((int64_t)b * Tmax + t_off + t_new) * tok + g * D + lane * 8) =
@@ -932,12 +943,13 @@ decode_wide_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const _
                     if (whole) {
                         const f32x4_t x = o * inv;
                         u32x2_t u = {pack2<T>(x[0], x[1]), pack2<T>(x[2], x[3])};
-                        *reinterpret_cast<u32x2_t *>(out + (row0 + col) * D + kb * 4 + dt * 16) = u;
-                    } else {
+                        if (GQA_IN_RANGE(row0 + col, (int64_t)B * H, 8))
+                            *reinterpret_cast<u32x2_t *>(out + (row0 + col) * D + kb * 4 + dt * 16) = u;
+                    } else if (GQA_IN_RANGE(slot + col, (int64_t)(nwg + B) * H, 8)) {
                         *reinterpret_cast<f32x4_t *>(part + (slot + col) * D + kb * 4 + dt * 16) = o * inv;
                     }
                 }
-                if (!whole && kb == 0)
+                if (!whole && kb == 0 && GQA_IN_RANGE(slot + col, (int64_t)(nwg + B) * H, 8))
                     lse[slot + col] = Ls > 0.f ? M + fast_log2(Ls) : -INFINITY;
             }
             __syncthreads();  // the next piece's loads refill the stages
@@ -998,7 +1010,7 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
     __bf16 *dst = out + ((int64_t)b * H + h) * D + d0;
     const int L = b < 64 ? __builtin_amdgcn_readlane(L_first, b) : seq_span(seqlens[b], Tmax, append, window).n;
     if (L == 0) {
-        if (sl == 0)
+        if (sl == 0 && GQA_IN_RANGE((int64_t)b * H + h, (int64_t)B * H, 10))
             *reinterpret_cast<u32x2_t *>(dst) = (u32x2_t){0, 0};
         return;
     }
@@ -1018,8 +1030,9 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
         for (int u = 0; u < U; ++u) {
             const int j = min(j0 + NS * u, nslots - 1);
             const int64_t idx = (k_first + j + b) * H + h;  // slot of piece k_first + j
-            x[u] = lse[idx];
-            pv[u] = *reinterpret_cast<const f32x4_t *>(part + idx * D + d0);
+            const bool ok = GQA_IN_RANGE(idx, (int64_t)(nwg + B) * H, 9);
+            x[u] = ok ? lse[idx] : -INFINITY;
+            pv[u] = ok ? *reinterpret_cast<const f32x4_t *>(part + idx * D + d0) : (f32x4_t){0.f, 0.f, 0.f, 0.f};
         }
         // All loads of the round are issued before any is used (the compiler
         // otherwise sinks the last one into the branch that uses it, behind a
@@ -1057,7 +1070,7 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
         for (int e = 0; e < 4; ++e)
             num[e] += __shfl_xor(num[e], s, 64);
     }
-    if (sl == 0) {
+    if (sl == 0 && GQA_IN_RANGE((int64_t)b * H + h, (int64_t)B * H, 10)) {
         const float inv = 1.f / den;
         u32x2_t u = {pack2<T>(num[0] * inv, num[1] * inv), pack2<T>(num[2] * inv, num[3] * inv)};
         *reinterpret_cast<u32x2_t *>(dst) = u;
@@ -1113,6 +1126,8 @@ decode_f32_kernel(const float *__restrict__ q, float *kc, float *vc, const float
     }
     float m = -INFINITY, l = 0.f;
     for (int t = 0; t < L; ++t) {
+        if (t != t_new && !GQA_IN_RANGE(sp.lo + t, Tmax, 11))
+            continue;
         const int64_t off = (((int64_t)b * Tmax + sp.lo + t) * G + g) * D;
         const float *kp = (t == t_new) ? knew + new_off : kc + off;
         const float *vp = (t == t_new) ? vnew + new_off : vc + off;
@@ -1133,7 +1148,7 @@ decode_f32_kernel(const float *__restrict__ q, float *kc, float *vc, const float
 #pragma unroll
     for (int j = 0; j < J; ++j)
         out[row * D + lane + 64 * j] = L > 0 ? acc[j] / l : 0.f;
-    if (t_new >= 0 && h % r == 0) {  // the group's first head stores the appended token
+    if (t_new >= 0 && h % r == 0 && GQA_IN_RANGE(sp.lo + t_new, Tmax, 2)) {  // the group's first head stores the appended token
         const int64_t off = (((int64_t)b * Tmax + sp.lo + t_new) * G + g) * D;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
@@ -1273,5 +1288,7 @@ hipError_t launch_decode(const DecodePlan &p, const DecodeArgs &a, gqa_dtype dty
         return launch_split<__bf16, DD, NTT, WW, GG>(p, a);
     });
 }
+
+GQA_DEBUG_READER(debug_take_decode)
 
 }  // namespace gqa

@@ -243,4 +243,43 @@ __device__ __forceinline__ void compiler_fence()
     asm volatile("" ::: "memory");
 }
 
+// Debug builds (-DGQA_DEBUG): range checks at the kernels' global memory
+// accesses. A failed check sets bit `site` of this source file's violation
+// word and the access is skipped (a load gives zeros), so an indexing
+// mistake shows up as a flag that the host reads back (gqa_debug_checks)
+// instead of as a memory fault. Release builds compile the checks away.
+// Each source file that includes this header has its own word and defines
+// its reader with GQA_DEBUG_READER(name).
+#ifdef GQA_DEBUG
+static __device__ unsigned int gqa_debug_word;
+
+__device__ __forceinline__ bool debug_in_range(int64_t i, int64_t n, int site)
+{
+    if (i >= 0 && i < n)
+        return true;
+    atomicOr(&gqa_debug_word, 1u << site);
+    return false;
+}
+
+#define GQA_IN_RANGE(i, n, site) ::gqa::debug_in_range((int64_t)(i), (int64_t)(n), (site))
+// Host reader: copies this file's word to *w and clears it (synchronous).
+#define GQA_DEBUG_READER(name)                                                                 \
+    hipError_t name(unsigned int *w)                                                           \
+    {                                                                                          \
+        hipError_t e = hipMemcpyFromSymbol(w, HIP_SYMBOL(gqa_debug_word), sizeof(unsigned int)); \
+        if (e != hipSuccess)                                                                   \
+            return e;                                                                          \
+        const unsigned int zero = 0;                                                           \
+        return hipMemcpyToSymbol(HIP_SYMBOL(gqa_debug_word), &zero, sizeof zero);              \
+    }
+#else
+#define GQA_IN_RANGE(i, n, site) true
+#define GQA_DEBUG_READER(name)        \
+    hipError_t name(unsigned int *w)  \
+    {                                 \
+        *w = 0;                       \
+        return hipSuccess;            \
+    }
+#endif
+
 }  // namespace gqa

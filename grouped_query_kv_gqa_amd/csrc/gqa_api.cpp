@@ -343,4 +343,41 @@ int gqa_abi_version(void)
     return 2;
 }
 
+gqa_status gqa_debug_checks(int *enabled, uint32_t *flags)
+{
+#ifdef GQA_DEBUG
+    constexpr int on = 1;
+#else
+    constexpr int on = 0;
+#endif
+    if (enabled)
+        *enabled = on;
+    uint32_t f = 0;
+    if (on) {
+        hipError_t e = hipDeviceSynchronize();
+        unsigned int w = 0;
+        if (e == hipSuccess && (e = gqa::debug_take_decode(&w)) == hipSuccess)
+            f |= w & 0xffffu;
+        if (e == hipSuccess && (e = gqa::debug_take_prefill(&w)) == hipSuccess)
+            f |= (w & 0xffu) << 16;
+        if (e == hipSuccess && (e = gqa::debug_take_pool(&w)) == hipSuccess)
+            f |= (w & 0xffu) << 24;
+        if (e != hipSuccess)
+            return hip_failure(e, "debug check words");
+    }
+    if (flags)
+        *flags = f;
+    return GQA_OK;
+}
+
+gqa_status gqa_debug_selftest(hipStream_t stream)
+{
+    const hipError_t e = gqa::debug_selftest(stream);
+    if (e == hipErrorNotSupported)
+        return record(GQA_ERR_UNSUPPORTED, "range checks are compiled only into libgqa_debug.so");
+    if (e != hipSuccess)
+        return hip_failure(e, "debug self-test launch");
+    return GQA_OK;
+}
+
 }  // extern "C"

@@ -41,4 +41,13 @@ hipError_t launch_prefill(const PrefillArgs &args, gqa_dtype dtype);
 hipError_t launch_mean_pool(const void *in, const float *weights, int64_t N, int H, int G, int D, gqa_dtype dtype,
                             void *out, hipStream_t stream);
 
+// Debug builds: each kernel source file's range-check violation word (see
+// GQA_IN_RANGE in device_common.h), read and cleared; 0 in release builds.
+hipError_t debug_take_decode(unsigned int *w);
+hipError_t debug_take_prefill(unsigned int *w);
+hipError_t debug_take_pool(unsigned int *w);
+// Debug builds: one range check that fails on purpose, guarding no memory
+// access (pooling word, bit 7); hipErrorNotSupported in release builds.
+hipError_t debug_selftest(hipStream_t stream);
+
 }  // namespace gqa

@@ -77,6 +77,8 @@ mean_pool_kernel(const T *__restrict__ in, const float *__restrict__ w, int64_t 
         const int g = (int)(ng % G);
         const int64_t n = ng / G;
         const T *src = in + (n * H + (int64_t)g * r) * D + c * 8;
+        if (!(GQA_IN_RANGE(n * H + (int64_t)g * r + r - 1, N * H, 0) && GQA_IN_RANGE(ng, N * G, 1)))
+            continue;
         float acc[8], x[8];
         Chunk8<T>::load(src, acc);
         if constexpr (WEIGHTED) {
@@ -135,5 +137,30 @@ hipError_t launch_mean_pool(const void *in, const float *weights, int64_t N, int
         launch_pool_t<__bf16>(in, weights, N, H, G, D, out, stream);
     return hipGetLastError();
 }
+
+#ifdef GQA_DEBUG
+namespace {
+// One range check that fails by construction (index n of n) and guards no
+// memory access: it only sets its flag.
+__global__ void debug_selftest_kernel(int n)
+{
+    if (threadIdx.x == 0)
+        (void)GQA_IN_RANGE(n, n, 7);
+}
+}  // namespace
+#endif
+
+hipError_t debug_selftest(hipStream_t stream)
+{
+#ifdef GQA_DEBUG
+    debug_selftest_kernel<<<1, 64, 0, stream>>>(1);
+    return hipGetLastError();
+#else
+    (void)stream;
+    return hipErrorNotSupported;
+#endif
+}
+
+GQA_DEBUG_READER(debug_take_pool)
 
 }  // namespace gqa

@@ -110,6 +110,8 @@ prefill_row_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
     }
     float m = -INFINITY, l = 0.f;
     for (int s = s0; s < nkeys; ++s) {
+        if (!GQA_IN_RANGE(s, T_, 3))
+            continue;
         const int64_t off = ((b * T_ + s) * G + g) * D;
         float dot = 0.f;
 #pragma unroll
@@ -249,7 +251,7 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
         u32x4_t x = {0, 0, 0, 0};
-        if (row_ok)
+        if (row_ok && GQA_IN_RANGE(qrow, (int64_t)gridDim.z * T * H, 0))
             x = ld16(q + qrow * D + ks * 16 + h * 8);
         qf[ks] = __builtin_bit_cast(bf16x8_t, x);
     }
@@ -286,8 +288,9 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         const int row0 = tile * kPfBN;
         const __bf16 *base = src + ((int64_t)b * T + row0) * G * D;
         const int nrec = (min(T, row0 + kPfBN) - row0) * tok_bytes;
-        buffer_rows_to_lds<C::LOADS>(base, nrec, dst + wave * C::WAVE_ROWS * D, kPfWaves * C::WAVE_ROWS * D,
-                                     is_v ? voff_v : voff_k, kPfWaves * C::WAVE_ROWS * tok_bytes);
+        if (GQA_IN_RANGE(row0, T, 1) && GQA_IN_RANGE(b, gridDim.z, 1))
+            buffer_rows_to_lds<C::LOADS>(base, nrec, dst + wave * C::WAVE_ROWS * D, kPfWaves * C::WAVE_ROWS * D,
+                                         is_v ? voff_v : voff_k, kPfWaves * C::WAVE_ROWS * tok_bytes);
     };
 
     // LDS fragment addresses. The swizzles only permute chunks inside a
@@ -615,7 +618,7 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
 
     // Epilogue: lane holds O^T[dt*32 + 8*m0 + 4*h + m1][row]; 4 consecutive d per (dt, m0).
     const float lsum = xor_add<32>(l_run);
-    if (!row_ok)
+    if (!row_ok || !GQA_IN_RANGE(qrow, (int64_t)gridDim.z * T * H, 2))
         return;
     const float inv = 1.f / lsum;
     __bf16 *dst = out + qrow * D + 4 * h;
@@ -662,5 +665,7 @@ hipError_t launch_prefill(const PrefillArgs &a, gqa_dtype dtype)
         return launch_16bit<_Float16>(a);
     return launch_16bit<__bf16>(a);
 }
+
+GQA_DEBUG_READER(debug_take_prefill)
 
 }  // namespace gqa

@@ -274,6 +274,31 @@ gqa_status gqa_release_workspaces(void);
 /* Library ABI version: 2. */
 int gqa_abi_version(void);
 
+/*
+ * gqa_debug_checks -- the device range checks of a debug build.
+ * libgqa_debug.so is the same library compiled with -DGQA_DEBUG: every
+ * kernel checks the index of each global-memory access (cache positions
+ * against Tmax, rows against B*H or B*T*H, partial-row slots against the
+ * workspace, tile rows against T) and, on a failure, sets a flag and skips
+ * the access instead of faulting. This call waits for the current device to
+ * go idle, then writes to *flags the flags raised on it since the previous
+ * call (bits 0-15 decode and merge kernels, 16-23 prefill, 24-31 pooling;
+ * 0: no violation) and clears them; *enabled = 1. In the release library
+ * (libgqa.so) the checks are compiled out: *enabled = 0, *flags = 0, and
+ * nothing waits. Either pointer may be NULL. GQA_ERR_HIP if the wait or the
+ * flag copies fail.
+ */
+gqa_status gqa_debug_checks(int *enabled, uint32_t *flags);
+
+/*
+ * gqa_debug_selftest -- debug library only: queues on `stream` one range
+ * check that fails by construction and guards no memory access, so that the
+ * next gqa_debug_checks reports bit 31 (pooling word, bit 7). Lets a caller
+ * confirm that violations reach the host. GQA_ERR_UNSUPPORTED in the release
+ * library (nothing queued).
+ */
+gqa_status gqa_debug_selftest(hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,6 +32,23 @@ def test_header_symbols_exported():
         assert re.search(rf"\bT {n}\b", out), f"{n} not a defined text symbol"
 
 
+def test_debug_library_exports_the_same_symbols():
+    # libgqa_debug.so: the same sources with device range checks compiled in
+    dbg = os.path.join(os.path.dirname(gq.library_path()), "libgqa_debug.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", dbg], capture_output=True, text=True).stdout
+    for n in _declared():
+        assert re.search(rf"\bT {n}\b", out), f"{n} not defined in libgqa_debug.so"
+
+
+def test_release_library_has_no_debug_checks():
+    lib = gq.load_library()
+    en, fl = ctypes.c_int(-1), ctypes.c_uint32(7)
+    assert lib.gqa_debug_checks(ctypes.byref(en), ctypes.byref(fl)) == gq.GQA_OK
+    assert (en.value, fl.value) == (0, 0)
+    assert lib.gqa_debug_checks(None, None) == gq.GQA_OK
+    assert lib.gqa_debug_selftest(None) == gq.GQA_ERR_UNSUPPORTED
+
+
 def test_status_strings():
     lib = gq.load_library()
     assert lib.gqa_status_string(0) == b"ok"
