@@ -963,11 +963,11 @@ decode_wide_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const _
 // Merge of the partial rows. Workgroup = (block of 4 row items, sequence b):
 // its 256 threads compute the partition once; each wave then merges one item
 // = (head h, NQ*4 consecutive d). Lanes form 64/NQ slot lanes x NQ d-quads:
-// slot lane sl takes the row's pieces sl, sl + 64/NQ, ... and the lanes of a
-// d-quad are combined with shuffles. out = sum_j w_j o_j with
+// slot lane sl takes the row's pieces sl, sl + 64/NQ, ... (U per round) and
+// the lanes of a d-quad are combined with shuffles. out = sum_j w_j o_j with
 // w_j = 2^(lse_j - M) / sum_j' 2^(lse_j' - M). Also writes the zero rows of
 // empty sequences; rows that the decode kernel wrote whole are skipped.
-template <typename T, int D, int NQ>
+template <typename T, int D, int NQ, int U>
 __global__ void __launch_bounds__(256)
 decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax, int append, int window, int nwg,
                     int fixed_P, int startup, const float *part, const float *lse, __bf16 *__restrict__ out)
@@ -1022,7 +1022,7 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
 
     float m = -INFINITY, den = 0.f;
     f32x4_t num = {0.f, 0.f, 0.f, 0.f};
-    constexpr int U = 4;  // slots per lane per round, loads issued together
+    // U slots per lane per round, loads issued together
     for (int j0 = sl; j0 < nslots; j0 += NS * U) {
         float x[U];
         f32x4_t pv[U];
@@ -1077,12 +1077,12 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
     }
 }
 
-template <typename T, int D, int NQ>
+template <typename T, int D, int NQ, int U>
 hipError_t launch_merge(const DecodePlan &p, const DecodeArgs &a)
 {
     constexpr int NDC = D / (4 * NQ);
     dim3 grid((unsigned)((a.H * NDC + 3) / 4), (unsigned)a.B);
-    decode_merge_kernel<T, D, NQ><<<grid, 256, 0, a.stream>>>(a.seqlens, a.B, a.H, a.Tmax, a.knew != nullptr,
+    decode_merge_kernel<T, D, NQ, U><<<grid, 256, 0, a.stream>>>(a.seqlens, a.B, a.H, a.Tmax, a.knew != nullptr,
                                                           a.window, p.nwg, p.fixed_P, p.startup, a.part, a.lse,
                                                           static_cast<__bf16 *>(a.out));
     return hipGetLastError();
@@ -1091,13 +1091,20 @@ hipError_t launch_merge(const DecodePlan &p, const DecodeArgs &a)
 template <typename T, int D>
 hipError_t launch_merge_d(const DecodePlan &p, const DecodeArgs &a)
 {
+    if (p.merge_u == 16) {  // rows of more than 128 pieces: at least 16 slot lanes
+        switch (p.merge_nq) {
+        case 1: return launch_merge<T, D, 1, 16>(p, a);
+        case 2: return launch_merge<T, D, 2, 16>(p, a);
+        default: return launch_merge<T, D, 4, 16>(p, a);
+        }
+    }
     switch (p.merge_nq) {
-    case 1: return launch_merge<T, D, 1>(p, a);
-    case 2: return launch_merge<T, D, 2>(p, a);
-    case 4: return launch_merge<T, D, 4>(p, a);
-    case 8: return launch_merge<T, D, 8>(p, a);
-    case 16: return launch_merge<T, D, 16>(p, a);
-    default: return launch_merge<T, D, (D >= 128 ? 32 : 16)>(p, a);
+    case 1: return launch_merge<T, D, 1, 4>(p, a);
+    case 2: return launch_merge<T, D, 2, 4>(p, a);
+    case 4: return launch_merge<T, D, 4, 4>(p, a);
+    case 8: return launch_merge<T, D, 8, 4>(p, a);
+    case 16: return launch_merge<T, D, 16, 4>(p, a);
+    default: return launch_merge<T, D, (D >= 128 ? 32 : 16), 4>(p, a);
     }
 }
 

@@ -26,6 +26,7 @@ struct DecodePlan {
     int full_P = 32;     // piece length when every sequence has Tmax positions
     int startup = 0;     // virtual positions before each sequence (the cost of starting a piece); 0 with fixed_P
     int merge_nq = 8;    // merge kernel: d-quads per wave (64/merge_nq lanes share a quad)
+    int merge_u = 4;     // merge kernel: pieces each slot lane loads per round (4 or 16)
     int64_t part_offset = 0;      // fp32 partial rows [nwg + B][H][d_h]
     int64_t lse_offset = 0;       // fp32 base-2 log-sum-exp [nwg + B][H]
     int64_t workspace_bytes = 0;  // 0 for the fp32 path
