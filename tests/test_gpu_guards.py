@@ -105,17 +105,19 @@ def test_decode_step_guard_bands(dtype, window):
     assert np.array_equal(_bits(kc), _bits(ref_k)) and np.array_equal(_bits(vc), _bits(ref_v)), "cache contents"
 
 
-@pytest.mark.parametrize("B,T,H,G,D,dtype,window", [
+_PREFILL_GUARD = [
     (2, 97, 8, 2, 128, torch.bfloat16, 0),
     (1, 200, 32, 8, 128, torch.bfloat16, 0),
     (1, 130, 64, 1, 128, torch.float16, 0),
     (2, 150, 16, 4, 64, torch.bfloat16, 40),
     (1, 40, 6, 3, 64, torch.float32, 0),
-])
-@pytest.mark.parametrize("causal", [True, False])
+]
+
+
+# every shape causal, and without a window also full attention (a window needs the causal mask)
+@pytest.mark.parametrize("B,T,H,G,D,dtype,window,causal",
+                         [c + (True,) for c in _PREFILL_GUARD] + [c + (False,) for c in _PREFILL_GUARD if not c[-1]])
 def test_prefill_out_guard_bands(B, T, H, G, D, dtype, window, causal):
-    if window and not causal:
-        pytest.skip("a window needs a causal mask")
     say(f"prefill guard bands B={B} T={T} H={H} G={G} D={D} {dtype} window={window} causal={causal}")
     w = I.PrefillWorkload("guard", B, T, H, G, D, dtype, causal)
     x = I.prefill_inputs(w, seed=T + H, device=DEV)
