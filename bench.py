@@ -16,7 +16,8 @@ under "prefill" in TFLOP/s (2*B*H*T^2*d_h per call) against the dense bf16
 MFMA peak, and "next" times the adjacent rows (fused append, sliding
 windows, fp16, weighted pooling). "copy_ceiling" measures plain streaming
 read and copy kernels over 1 GiB as the practical bandwidth ceiling next to
-the 8 TB/s peak.
+the 8 TB/s peak, and each decode workload's roofline carries "plain_read",
+the same plain read over that workload's bytes and input rotation.
 
 Inputs are synthetic (seeded N(0,1), no datasets or weights) and resident in
 HBM before timing starts. A workload whose cache is below 1 GiB rotates
@@ -213,6 +214,10 @@ def run_decode(key, w, args, steps, warmup):
                                               "p10": round(pct(per, 0.1), 5), "p90": round(pct(per, 0.9), 5)}},
         },
     }
+    if not args.no_plain_read:
+        rc = plain_read(byts, ncopy, args)
+        rc["decode_over_plain_read"] = round(gbs / rc["GBs"], 4)
+        entry["roofline"]["plain_read"] = rc
     return entry, xs[0], wall
 
 
@@ -246,21 +251,58 @@ def run_prefill(args):
     return entry, x
 
 
+_PROBE = None
+
+
+def _probe_lib():
+    global _PROBE
+    if _PROBE is None:
+        import ctypes
+        from grouped_query_kv_gqa_amd import build as gbuild
+        lib = ctypes.CDLL(gbuild.PROBE_LIB)
+        lib.gqa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        lib.gqa_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        lib.gqa_probe_read.restype = lib.gqa_probe_copy.restype = ctypes.c_int
+        lib.gqa_probe_threads.restype = ctypes.c_int
+        _PROBE = lib
+    return _PROBE
+
+
+def plain_read(nbytes: int, copies: int, args, steps: int = 200):
+    """A reference at one workload's size: the probe's plain nontemporal
+    streaming read of the same byte count (rounded up to 32 KiB), rotating
+    through as many buffers as the workload has input copies, timed like the
+    workload (warmup, settle, one event pair around `steps` reads). It is a
+    simple kernel (2048 workgroups, each a contiguous slice), not a bound:
+    the decode kernels beat it on the largest cache."""
+    import torch
+    lib = _probe_lib()
+    n = (nbytes + 32767) // 32768 * 32768
+    bufs = [torch.ones(n // 4, dtype=torch.int32, device="cuda") for _ in range(copies)]
+    sink = torch.empty(lib.gqa_probe_threads(), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def read(i):
+        if lib.gqa_probe_read(bufs[i % copies].data_ptr(), n, 1, sink.data_ptr(), stream.cuda_stream) != 0:
+            raise RuntimeError("bandwidth probe failed")
+
+    _, mean_ms, _, _ = timed_calls(read, steps, 10, args.settle_ms, stream)
+    del bufs, sink
+    torch.cuda.empty_cache()
+    gbs = nbytes / (mean_ms * 1e-3) / 1e9
+    return {"kernel": "plain nontemporal streaming read of the same bytes, same rotation",
+            "us": round(mean_ms * 1e3, 2), "GBs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def copy_ceiling(args):
     """Practical HBM ceiling: plain streaming kernels (libgqa_probe.so) over a
     1 GiB buffer, 2048 workgroups of 256 threads, 16-byte loads, four in
     flight per thread: a read with the default and the nontemporal cache
     policy, and a copy (2 GiB moved). Best and median of 10 event-timed calls
     after 3 warmup calls."""
-    import ctypes
     import torch
-    from grouped_query_kv_gqa_amd import build as gbuild
 
-    lib = ctypes.CDLL(gbuild.PROBE_LIB)
-    lib.gqa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    lib.gqa_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
-    lib.gqa_probe_read.restype = lib.gqa_probe_copy.restype = ctypes.c_int
-    lib.gqa_probe_threads.restype = ctypes.c_int
+    lib = _probe_lib()
     n = 1 << 30
     a = torch.ones(n // 4, dtype=torch.int32, device="cuda")
     b = torch.empty_like(a)
@@ -489,6 +531,8 @@ def main():
                     help="after the warmup calls, keep calling for at least this long before timing")
     # 200 calls: the host's latency in launching the first call of the timed
     # region (the GPU idles until it arrives) stays under 1% of a 38 us call
+    ap.add_argument("--no-plain-read", action="store_true",
+                    help="skip the plain read of each decode workload's bytes (a reference at its size)")
     ap.add_argument("--config-steps", type=int, default=200, help="timed calls of every other decode workload")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--prefill-warmup", type=int, default=3)
