@@ -4,7 +4,7 @@ point, storage type and edge length (empty, negative and over-long seqlens,
 full caches, windows wider and narrower than the sequence, listed prefill
 rows). Every buffer is its own heap allocation of exactly the documented
 size, so a read or write past any of them, a double free or a leak fails the
-run; the driver also checks a few exact properties on the way (rows sum to
+run; the C program also checks a few exact properties on the way (rows sum to
 one, one cached position returns its value row, the append writes exactly
 one cache row)."""
 import os
