@@ -174,7 +174,7 @@ def decode(q, k_cache, v_cache, seqlens, scale: float | None = None, out=None, s
         if out.shape != q.shape or out.dtype != q.dtype or out.device != dev:
             raise ValueError("out must match q")
     if scale is None:
-        scale = D ** -0.5
+        scale = float("nan")  # the library's default, 1/sqrt(d_h)
     with torch.cuda.device(dev):
         _check(lib.gqa_decode_ex(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr(),
                                  B, H, G, D, Tmax, float(scale), _dtype_code(q), out.data_ptr(),
@@ -215,7 +215,7 @@ def decode_step(q, k_cache, v_cache, seqlens, scale: float | None = None, k_new=
         if out.shape != q.shape or out.dtype != q.dtype or out.device != dev:
             raise ValueError("out must match q")
     if scale is None:
-        scale = D ** -0.5
+        scale = float("nan")  # the library's default, 1/sqrt(d_h)
     kn = k_new.data_ptr() if k_new is not None else None
     vn = v_new.data_ptr() if v_new is not None else None
     with torch.cuda.device(dev):

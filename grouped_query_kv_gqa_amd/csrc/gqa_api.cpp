@@ -7,6 +7,7 @@
 // workspace.cpp), and cached device properties.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <mutex>
 #include <string>
 #include <unordered_map>
@@ -137,6 +138,8 @@ gqa_status decode_impl(const void *q, const void *k_new, const void *v_new, cons
         return record(s, err);
     if (split_tokens < 0)
         return record(GQA_ERR_INVALID_ARG, "split_tokens must be >= 0");
+    if (std::isnan(scale))
+        scale = 1.0f / std::sqrt((float)d_h);
     gqa::DecodePlan plan;
     // sizes and launch limits, before anything touches the runtime
     if ((s = gqa::plan_decode(B, H, G, d_h, Tmax, dtype, split_tokens, 0, 0, &plan, &err)) != GQA_OK)

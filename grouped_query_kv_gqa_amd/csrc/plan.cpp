@@ -66,8 +66,8 @@ gqa_status check_decode(const void *q, const void *k, const void *v, const int32
         return fail(err, GQA_ERR_UNSUPPORTED, "unknown dtype");
     if (d_h != 64 && d_h != 128)
         return fail(err, GQA_ERR_UNSUPPORTED, "d_h must be 64 or 128");
-    if (!std::isfinite(scale))
-        return fail(err, GQA_ERR_INVALID_ARG, "scale must be finite");
+    if (std::isinf(scale))  // NaN selects 1/sqrt(d_h)
+        return fail(err, GQA_ERR_INVALID_ARG, "scale must be finite (or NaN for 1/sqrt(d_h))");
     if (B == 0)
         return GQA_OK;
     if (!q || !seqlens || !out || (Tmax > 0 && (!k || !v)))

@@ -72,7 +72,7 @@ typedef enum gqa_dtype { GQA_BF16 = 0, GQA_FP32 = 1, GQA_FP16 = 2 } gqa_dtype;
  *            L_b = 0 gives an all-zero output row. Whether the newest token's
  *            key and value are among the L_b positions is the caller's choice.
  *   scale    multiplies q.k before the softmax (1/sqrt(d_h) for the pages'
- *            attention); must be finite.
+ *            attention); finite, or NaN to select 1/sqrt(d_h).
  *   out      [B, H, d_h]        same dtype as q
  *   out[b,h,:] = sum_t softmax_t(scale * q[b,h,:].k_cache[b,t,g(h),:]) v_cache[b,t,g(h),:]
  *

@@ -76,6 +76,7 @@ def test_decode_argument_checks():
     assert _decode(lib, D=96) == gq.GQA_ERR_UNSUPPORTED
     assert _decode(lib, dt=7) == gq.GQA_ERR_UNSUPPORTED
     assert _decode(lib, scale=float("inf")) == gq.GQA_ERR_INVALID_ARG
+    assert _decode(lib, scale=float("-inf")) == gq.GQA_ERR_INVALID_ARG  # NaN instead selects 1/sqrt(d_h)
     assert _decode(lib, q=None) == gq.GQA_ERR_INVALID_ARG
     assert _decode(lib, sl=None) == gq.GQA_ERR_INVALID_ARG
     assert _decode(lib, q=18) == gq.GQA_ERR_INVALID_ARG          # misaligned

@@ -303,3 +303,22 @@ def test_decode_wide_groups(B, H, G, D, Tmax, seqlens, dtype):
         assert_parity(out, ref_s, dtype, f"append window={window} split={split}")
         assert np.array_equal(to_host(kc).view(torch.int16).numpy().view(np.uint16), kr)
         assert np.array_equal(to_host(vc).view(torch.int16).numpy().view(np.uint16), vr)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_default_scale_is_inverse_sqrt_dh(D):
+    # no scale given: the library's default, 1/sqrt(d_h), bit for bit the same
+    # as passing it (both round to the same float)
+    say(f"decode default scale D={D}")
+    w = I.DecodeWorkload("scale", 3, 16, 4, D, 300, torch.bfloat16)
+    x = I.decode_inputs(w, seed=21, device=DEV, seqlens=[300, 17, 0])
+    a = gq.decode(x["q"], x["k_cache"], x["v_cache"], x["seqlens"])
+    b = gq.decode(x["q"], x["k_cache"], x["v_cache"], x["seqlens"], scale=D ** -0.5)
+    k0, v0 = x["k_cache"].clone(), x["v_cache"].clone()
+    kn = I.random_tensor((3, 4, D), seed=22, dtype=torch.bfloat16, device=DEV)
+    c = gq.decode_step(x["q"], k0, v0, x["seqlens"], k_new=kn, v_new=kn, window=64)
+    k1, v1 = x["k_cache"].clone(), x["v_cache"].clone()
+    d = gq.decode_step(x["q"], k1, v1, x["seqlens"], scale=D ** -0.5, k_new=kn, v_new=kn, window=64)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(c.view(torch.int16), d.view(torch.int16))
