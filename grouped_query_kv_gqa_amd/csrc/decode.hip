@@ -992,15 +992,18 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
         if (i == lane)
             L_first = Li;
     }
-    const int64_t tot = wave_total(tot_part);
-    const int64_t pre_b = wave_total(pre_part) + startup;
-    int64_t P;
+    // 32-bit arithmetic: flat positions stay below 2^31 (the host checks
+    // B * (Tmax + startup) < 2^31), and the slice length is the same as the
+    // decode kernels' (make_partition).
+    const uint32_t tot = (uint32_t)wave_total(tot_part);
+    const uint32_t pre_b = (uint32_t)wave_total(pre_part) + (uint32_t)startup;
+    uint32_t P;
     if (fixed_P > 0) {
-        P = fixed_P;
+        P = (uint32_t)fixed_P;
     } else {
-        P = (tot + nwg - 1) / nwg;
+        P = (tot + (uint32_t)nwg - 1) / (uint32_t)nwg;
         P = ((P + kTile - 1) / kTile) * kTile;
-        if (P < kTile)
+        if (P < (uint32_t)kTile)
             P = kTile;
     }
 
@@ -1015,7 +1018,7 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
         return;
     }
     const int64_t k_first = pre_b / P;
-    const int64_t k_last = (pre_b + L - 1) / P;
+    const int64_t k_last = (pre_b + (uint32_t)L - 1) / P;
     if (k_first == k_last)
         return;  // written whole by the decode kernel
     const int nslots = (int)(k_last - k_first + 1);
@@ -1055,21 +1058,33 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
             num += w * pv[u];
         }
     }
-    // combine the slot lanes of each d-quad (lanes qd, qd + NQ, ...)
-    float M = m;
-#pragma unroll
-    for (int s = 32; s >= NQ; s >>= 1)
-        M = wave_max_xor(M, s);
+    // combine the slot lanes of each d-quad (lanes qd, qd + NQ, ...), by
+    // lane exchanges on the VALU, masks 32, 16, ... down to NQ
+    auto over_slots = [&](float x, auto op) {
+        if constexpr (NQ <= 32)
+            x = op(x, Ic<32>{});
+        if constexpr (NQ <= 16)
+            x = op(x, Ic<16>{});
+        if constexpr (NQ <= 8)
+            x = op(x, Ic<8>{});
+        if constexpr (NQ <= 4)
+            x = op(x, Ic<4>{});
+        if constexpr (NQ <= 2)
+            x = op(x, Ic<2>{});
+        if constexpr (NQ <= 1)
+            x = op(x, Ic<1>{});
+        return x;
+    };
+    const auto vmax = [](float x, auto S) { return xor_fmax<decltype(S)::value>(x); };
+    const auto vsum = [](float x, auto S) { return xor_add<decltype(S)::value>(x); };
+    const float M = over_slots(m, vmax);
     const float f = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
     den *= f;
     num *= f;
+    den = over_slots(den, vsum);
 #pragma unroll
-    for (int s = 32; s >= NQ; s >>= 1) {
-        den += __shfl_xor(den, s, 64);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            num[e] += __shfl_xor(num[e], s, 64);
-    }
+    for (int e = 0; e < 4; ++e)
+        num[e] = over_slots(num[e], vsum);
     if (sl == 0 && GQA_IN_RANGE((int64_t)b * H + h, (int64_t)B * H, 10)) {
         const float inv = 1.f / den;
         u32x2_t u = {pack2<T>(num[0] * inv, num[1] * inv), pack2<T>(num[2] * inv, num[3] * inv)};

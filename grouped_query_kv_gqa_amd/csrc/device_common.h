@@ -128,32 +128,53 @@ __device__ __forceinline__ float wave_max_xor(float x, int mask)
     return fmaxf(x, __shfl_xor(x, mask, 64));
 }
 
-// x of this lane and of lane l ^ MASK (MASK = 16 or 32), exchanged by the
-// VALU lane swaps (v_permlane16_swap / v_permlane32_swap with both operands
-// x): `a`, `b` are the two values, in an order that differs between the two
-// lanes of a pair, so their maximum or sum is the same in both lanes. Unlike
-// __shfl_xor (ds_bpermute) the swap does not go through the LDS queue and
-// never waits behind outstanding LDS reads. Lane layout checked on gfx950.
-// The two results are copied to scalars before the bit casts: clang's
-// __builtin_bit_cast of a vector element expression reads the vector's first
-// element whatever the index.
+// x of this lane and of lane l ^ MASK, exchanged on the VALU: for MASK = 16
+// or 32 by the lane swaps (v_permlane16_swap / v_permlane32_swap with both
+// operands x), for MASK = 1, 2, 4 or 8 by DPP moves within rows of 16 lanes
+// (quad_perm for 1 and 2, row_ror:8 for 8, row_shl:4 or row_shr:4 by lane
+// for 4). `a`, `b` are the two values, in an order that may differ between
+// the two lanes of a pair, so their maximum or sum is the same in both
+// lanes. Unlike __shfl_xor (ds_bpermute) no exchange goes through the LDS
+// queue or waits behind outstanding LDS reads. Lane layout checked on
+// gfx950. The swap results are copied to scalars before the bit casts:
+// clang's __builtin_bit_cast of a vector element expression reads the
+// vector's first element whatever the index.
 template <int MASK>
 __device__ __forceinline__ void xor_pair(float x, float &a, float &b)
 {
-    static_assert(MASK == 16 || MASK == 32, "lane swaps exchange rows of 16 or halves of 32");
+    static_assert(MASK == 1 || MASK == 2 || MASK == 4 || MASK == 8 || MASK == 16 || MASK == 32,
+                  "lane exchanges for xor masks 1 to 32");
     const uint32_t u = __builtin_bit_cast(uint32_t, x);
-    uint32_t s0, s1;
-    if constexpr (MASK == 32) {
-        const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-        s0 = s[0];
-        s1 = s[1];
+    if constexpr (MASK >= 16) {
+        uint32_t s0, s1;
+        if constexpr (MASK == 32) {
+            const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+            s0 = s[0];
+            s1 = s[1];
+        } else {
+            const auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+            s0 = s[0];
+            s1 = s[1];
+        }
+        a = __builtin_bit_cast(float, s0);
+        b = __builtin_bit_cast(float, s1);
     } else {
-        const auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-        s0 = s[0];
-        s1 = s[1];
+        const int v = (int)u;
+        int p;
+        if constexpr (MASK == 1) {
+            p = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+        } else if constexpr (MASK == 2) {
+            p = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+        } else if constexpr (MASK == 8) {
+            p = __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+        } else {
+            const int up = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0xF, false);    // row_shl:4: lane + 4
+            const int down = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4: lane - 4
+            p = (__lane_id() & 4) ? down : up;
+        }
+        a = x;
+        b = __builtin_bit_cast(float, p);
     }
-    a = __builtin_bit_cast(float, s0);
-    b = __builtin_bit_cast(float, s1);
 }
 
 template <int MASK>
