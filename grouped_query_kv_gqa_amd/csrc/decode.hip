@@ -62,8 +62,8 @@ struct TileCfg {
     static constexpr int KS = D / 32;          // MFMA k-steps over d_h
     static constexpr int DT = D / 16;          // 16-wide d tiles of the output
     static constexpr int CH = D / 8;           // 16-byte chunks per row
-    static constexpr int VROWS = 64 / CH;      // V rows per coalesced load
-    static constexpr int VLOADS = kTile / VROWS;
+    static constexpr int VROWS = 64 / CH;      // K or V rows per coalesced load
+    static constexpr int VLOADS = kTile / VROWS;  // loads per K or V tile
     static constexpr int LDS_STRIDE = D + 16;  // padded row (elements): 4 rows cover all banks
     static constexpr int HEADS = 16 * NT;
 };
@@ -163,7 +163,8 @@ __device__ __forceinline__ uint64_t overlapping(int64_t pre, int incl, int L, in
 // their states (every wave of the workgroup must call this for the same
 // pieces: the combine has workgroup barriers). Writes the finished rows to
 // `out` when `whole`, else a normalised partial row per head and its base-2
-// log-sum-exp. `vl_all` is the workgroup's V-tile LDS, one tile per wave.
+// log-sum-exp. `vl_all` and `kl_all` are the workgroup's V-tile and K-tile
+// LDS, one tile of each per wave.
 //
 // APPEND: position t_new (relative to the span, or -1) is the appended token:
 // its rows come from knew_row/vnew_row (this group's slice of k_new, v_new)
@@ -173,11 +174,12 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
                                              int h0, int nheads, int t_off, int ta, int tb, int t_new,
                                              const __bf16 *knew_row, const __bf16 *vnew_row, bool store_new,
                                              bool whole, int H, int G, int Tmax, int sub, float scale_log2,
-                                             __bf16 *vl_all, __bf16 *__restrict__ out, float *__restrict__ part_row,
+                                             __bf16 *vl_all, __bf16 *kl_all, __bf16 *__restrict__ out, float *__restrict__ part_row,
                                              float *__restrict__ lse_row, int lane, bool store_ok)
 {
     const int wave = threadIdx.x >> 6;
     __bf16 *vl = vl_all + wave * kTile * TileCfg<D, NT>::LDS_STRIDE;  // this wave's V tile
+    __bf16 *kl = kl_all + wave * kTile * D;                            // this wave's K tile (swizzled)
     using C = TileCfg<D, NT>;
     const int col = lane & 15, kb = lane >> 4;
     const int64_t row0 = (int64_t)b * H + h0;
@@ -215,18 +217,23 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
     // row, and the values they bring are discarded below (scores set to -inf,
     // V rows replaced by zeros). Keeping per-lane branches away from loads
     // lets the compiler wait for exactly the data it needs.
+    //
+    // K and V both load whole row slices (the 64 lanes of one instruction
+    // cover 64/CH rows x the group's d_h*2 bytes) and both pass through this
+    // wave's LDS. K loaded straight into the MFMA A layout would take 16 rows
+    // x 64 bytes per instruction; measured on a plain read of this layout,
+    // that pattern streamed 6-8% slower (6.41 against 6.80 TB/s), and moving
+    // K through LDS took the ragged Llama-2-70B batch from 203.2 to 196.2 us.
     const int t_last = tb - 1;
-    auto load_k = [&](int t0, u32x4_t (&kr)[2][C::KS]) {
+    auto load_k = [&](int t0, u32x4_t (&kr)[C::VLOADS]) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const int t = min(t0 + mt * 16 + col, t_last);
+        for (int i = 0; i < C::VLOADS; ++i) {
+            const int t = min(t0 + i * C::VROWS + lane / C::CH, t_last);
             const __bf16 *src = kbase + t * tok_stride;
             if constexpr (APPEND)
                 src = (t == t_new) ? knew_row : src;
             const bool ok = (APPEND && t == t_new) || GQA_IN_RANGE(t_off + t, Tmax, 0);
-#pragma unroll
-            for (int s = 0; s < C::KS; ++s)
-                kr[mt][s] = ok ? load16_kv<NT == 1>(src + (s * 4 + kb) * 8) : (u32x4_t){0, 0, 0, 0};
+            kr[i] = ok ? load16_kv<NT == 1>(src + (lane % C::CH) * 8) : (u32x4_t){0, 0, 0, 0};
         }
     };
     auto load_v = [&](int t0, u32x4_t (&vr)[C::VLOADS]) {
@@ -252,30 +259,48 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
     const int stride = WPG * kTile;
     int t0 = ta + sub * kTile;
     const bool any_tile = t0 < tb;  // wave-uniform
-    u32x4_t kbuf[2][C::KS], vbuf[C::VLOADS];
+    u32x4_t kbuf[C::VLOADS], vbuf[C::VLOADS];
     if (any_tile) {
         load_k(t0, kbuf);
         load_v(t0, vbuf);
     }
-    auto tile = [&](u32x4_t (&kbf)[2][C::KS], u32x4_t (&vbf)[C::VLOADS], const int tc)
+    auto tile = [&](u32x4_t (&kbf)[C::VLOADS], u32x4_t (&vbf)[C::VLOADS], const int tc)
                     __attribute__((always_inline)) {
         const int tn = tc + stride;  // the tile these buffers take next
 
-        // S^T = K q^T for two 16-token row tiles.
+        // K tile into this wave's LDS rows, 16-byte chunk c of row r at slot
+        // c ^ (r mod CH), then the next K into the freed registers.
+#pragma unroll
+        for (int i = 0; i < C::VLOADS; ++i) {
+            const int tl = i * C::VROWS + lane / C::CH;
+            const int c = lane % C::CH;
+            *reinterpret_cast<u32x4_t *>(kl + tl * D + ((c ^ (tl % C::CH)) * 8)) = kbf[i];
+        }
+        compiler_fence();
+        __builtin_amdgcn_sched_barrier(0);
+        load_k(tn, kbf);  // clamped prefetch, also past the end
+        compiler_fence();
+        __builtin_amdgcn_sched_barrier(0);
+
+        // S^T = K q^T for two 16-token row tiles; A fragments from LDS.
         f32x4_t st[2][NT];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt) {
+            bf16x8_t kf[C::KS];
+#pragma unroll
+            for (int s = 0; s < C::KS; ++s) {
+                const int row = mt * 16 + col, ch = s * 4 + kb;
+                kf[s] = *reinterpret_cast<const bf16x8_t *>(kl + row * D + ((ch ^ (row % C::CH)) * 8));
+            }
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < C::KS; ++s)
-                    c = mfma16x16x32<T>(__builtin_bit_cast(bf16x8_t, kbf[mt][s]), qf[nt][s], c);
+                    c = mfma16x16x32<T>(kf[s], qf[nt][s], c);
                 st[mt][nt] = c;
             }
-        compiler_fence();
-        __builtin_amdgcn_sched_barrier(0);
-        load_k(tn, kbf);  // clamped prefetch, also past the end
+        }
         compiler_fence();
         __builtin_amdgcn_sched_barrier(0);
 
@@ -465,6 +490,7 @@ decode_split_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const 
     constexpr int WPG = WAVES / GB;
     using C = TileCfg<D, NT>;
     __shared__ __attribute__((aligned(16))) __bf16 vlds[WAVES][kTile * C::LDS_STRIDE];
+    __shared__ __attribute__((aligned(16))) __bf16 klds[WAVES][kTile * D];
 
     const int k = blockIdx.x;
     const int gblk = blockIdx.y / head_tiles;
@@ -532,7 +558,7 @@ decode_split_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const 
                                   (whole || GQA_IN_RANGE(slot + nheads - 1, (int64_t)(nwg + B) * H, 5));
             decode_piece<T, D, NT, WPG, APPEND>(q, kc, vc, b, g, h0, nheads, lo_b, ta, tb, t_new, knew + new_off,
                                              vnew + new_off, ht == 0, whole, H, G, Tmax, sub, scale_log2,
-                                             &vlds[0][0], out, part + slot * D, lse + slot, lane, store_ok);
+                                             &vlds[0][0], &klds[0][0], out, part + slot * D, lse + slot, lane, store_ok);
         }
         if (pre + chunk_total >= hi)
             return;
