@@ -261,8 +261,9 @@ def _probe_lib():
         from grouped_query_kv_gqa_amd import build as gbuild
         lib = ctypes.CDLL(gbuild.PROBE_LIB)
         lib.gqa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        lib.gqa_probe_read_wide.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
         lib.gqa_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
-        lib.gqa_probe_read.restype = lib.gqa_probe_copy.restype = ctypes.c_int
+        lib.gqa_probe_read.restype = lib.gqa_probe_read_wide.restype = lib.gqa_probe_copy.restype = ctypes.c_int
         lib.gqa_probe_threads.restype = ctypes.c_int
         _PROBE = lib
     return _PROBE
@@ -272,9 +273,9 @@ def plain_read(nbytes: int, copies: int, args, steps: int = 200):
     """A reference at one workload's size: the probe's plain nontemporal
     streaming read of the same byte count (rounded up to 32 KiB), rotating
     through as many buffers as the workload has input copies, timed like the
-    workload (warmup, settle, one event pair around `steps` reads). It is a
-    simple kernel (2048 workgroups, each a contiguous slice), not a bound:
-    the decode kernels beat it on the largest cache."""
+    workload (warmup, settle, one event pair around `steps` reads). The read
+    is the probe's faster one (one 8-wave workgroup per compute unit, 128 KiB
+    per workgroup in flight); a reference, not a bound."""
     import torch
     lib = _probe_lib()
     n = (nbytes + 32767) // 32768 * 32768
@@ -283,23 +284,25 @@ def plain_read(nbytes: int, copies: int, args, steps: int = 200):
     stream = torch.cuda.current_stream()
 
     def read(i):
-        if lib.gqa_probe_read(bufs[i % copies].data_ptr(), n, 1, sink.data_ptr(), stream.cuda_stream) != 0:
+        if lib.gqa_probe_read_wide(bufs[i % copies].data_ptr(), n, sink.data_ptr(), stream.cuda_stream) != 0:
             raise RuntimeError("bandwidth probe failed")
 
     _, mean_ms, _, _ = timed_calls(read, steps, 10, args.settle_ms, stream)
     del bufs, sink
     torch.cuda.empty_cache()
     gbs = nbytes / (mean_ms * 1e-3) / 1e9
-    return {"kernel": "plain nontemporal streaming read of the same bytes, same rotation",
+    return {"kernel": "plain nontemporal streaming read of the same bytes, same rotation "
+                      "(256 workgroups x 512 threads, 16 loads of 16 bytes in flight per thread)",
             "us": round(mean_ms * 1e3, 2), "GBs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def copy_ceiling(args):
     """Practical HBM ceiling: plain streaming kernels (libgqa_probe.so) over a
-    1 GiB buffer, 2048 workgroups of 256 threads, 16-byte loads, four in
-    flight per thread: a read with the default and the nontemporal cache
-    policy, and a copy (2 GiB moved). Best and median of 10 event-timed calls
-    after 3 warmup calls."""
+    1 GiB buffer: 2048 workgroups of 256 threads with four 16-byte loads in
+    flight per thread, reading with the default and the nontemporal cache
+    policy, and copying (2 GiB moved); and the wide read, 256 workgroups of
+    512 threads with sixteen nontemporal loads in flight per thread. Best and
+    median of 10 event-timed calls after 3 warmup calls."""
     import torch
 
     lib = _probe_lib()
@@ -329,10 +332,12 @@ def copy_ceiling(args):
         return ts[0], ts[len(ts) // 2]
 
     res = {"bytes": n, "peak_GBs": HBM_PEAK_GBS,
-           "kernel": "plain streaming read / copy, 2048 workgroups x 256 threads, 16-byte loads"}
+           "kernel": "plain streaming read / copy, 2048 workgroups x 256 threads, 16-byte loads; "
+                     "read_wide: 256 workgroups x 512 threads, 16 nontemporal loads in flight per thread"}
     for name, fn, moved in [
         ("read", lambda: call(lib.gqa_probe_read(a.data_ptr(), n, 0, sink.data_ptr(), stream.cuda_stream)), n),
         ("read_nt", lambda: call(lib.gqa_probe_read(a.data_ptr(), n, 1, sink.data_ptr(), stream.cuda_stream)), n),
+        ("read_wide", lambda: call(lib.gqa_probe_read_wide(a.data_ptr(), n, sink.data_ptr(), stream.cuda_stream)), n),
         ("copy", lambda: call(lib.gqa_probe_copy(b.data_ptr(), a.data_ptr(), n, stream.cuda_stream)), 2 * n),
     ]:
         best, med = timed(fn)
