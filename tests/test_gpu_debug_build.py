@@ -6,8 +6,9 @@ memory out of range.
 
 Every kernel family runs here from the debug library on shapes that reach its
 edges (empty, clamped and full sequences, appends, windows, sequences cut
-into many pieces, T not a multiple of the 64-position tile, groups wider than
-32 heads, the row kernels). No check may fire, and each result must equal the
+into many pieces or into slices long enough for the decode's falling wave
+priority, T not a multiple of the 64-position tile, groups wider than 32
+heads, the row kernels). No check may fire, and each result must equal the
 release library's bit for bit: the checks add branches, never arithmetic.
 Inputs come from the seeded generators of grouped_query_kv_gqa_amd.inputs.
 """
@@ -68,6 +69,7 @@ DECODE = [
     (70, 16, 4, 128, 96, [(7 * i) % 97 for i in range(70)], torch.bfloat16, 0),  # more than 64 sequences
     (2, 8, 8, 64, 200, [150, 200], torch.float16, 0),                  # multi-head, fp16
     (3, 12, 3, 64, 50, [50, 17, 0], torch.float32, 0),                 # fp32 path
+    (2, 16, 4, 128, 2000, [2000, 1500], torch.bfloat16, 1024),        # slices long enough for the wave priority
 ]
 
 
