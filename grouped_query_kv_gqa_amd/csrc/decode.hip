@@ -115,13 +115,20 @@ __device__ __forceinline__ Span seq_span(int32_t s, int Tmax, int append, int wi
 // starting a piece (first round trips, the combine at its end) in units of
 // positions: a workgroup whose range holds the start of a sequence then takes
 // that many fewer real positions, which evens out the workgroups' finishing
-// times. The host guarantees B * Tmax < 2^31 and bounds startup, so position
-// counts fit in 32 bits. `n_first` is this lane's span length among the
-// first 64 sequences (0 past B); the caller has read those lengths already
-// and keeps them for its walk.
+// times. A negative `startup` (the narrow kernel's default plan) asks for a
+// charge of -startup positions only where it leaves the tile-rounded slice
+// length unchanged, so that it never costs a workgroup: on the ragged
+// Llama-2-70B batch (P = 1152, 29 positions of rounding slack per slice) the
+// one-tile charge took 193.4 to 190.9 us; a uniform batch whose spans fill
+// the slices exactly (the Llama-3-8B layer, P = 256) keeps none. The host
+// guarantees B * (Tmax + |startup|) < 2^31, so position counts fit in 32
+// bits. `n_first` is this lane's span length among the first 64 sequences
+// (0 past B); the caller has read those lengths already and keeps them for
+// its walk. Every lane of the wave must call this (the counts use ballots).
 struct Partition {
     int64_t total;
     int64_t P;
+    int startup;  // the charge in effect
 };
 
 __device__ __forceinline__ int with_startup(int n, int startup)
@@ -129,23 +136,43 @@ __device__ __forceinline__ int with_startup(int n, int startup)
     return n > 0 ? n + startup : 0;
 }
 
+// Slice length for `tot` flat positions over nwg workgroups, in whole tiles
+// (32-bit: flat positions stay below 2^31).
+__device__ __forceinline__ uint32_t slice_positions(uint32_t tot, uint32_t nwg)
+{
+    uint32_t P = (tot + nwg - 1) / nwg;
+    P = ((P + kTile - 1) / kTile) * kTile;
+    return P < (uint32_t)kTile ? (uint32_t)kTile : P;
+}
+
 __device__ __forceinline__ Partition make_partition(int n_first, const int32_t *seqlens, int B, int Tmax, int append,
                                                     int window, int nwg, int fixed_P, int startup, int lane)
 {
-    int part = with_startup(n_first, startup);
-    for (int i = lane + 64; i < B; i += 64)
-        part += with_startup(seq_span(seqlens[i], Tmax, append, window).n, startup);
-    const int64_t tot = wave_total(part);
+    const int c0 = startup < 0 ? 0 : startup;
+    int part = with_startup(n_first, c0);
+    int nnz = __popcll(__ballot(n_first > 0));  // non-empty sequences (wave-uniform: every lane runs every chunk)
+    for (int i0 = 64; i0 < B; i0 += 64) {
+        const int i = i0 + lane;
+        const int n = i < B ? seq_span(seqlens[i], Tmax, append, window).n : 0;
+        part += with_startup(n, c0);
+        nnz += __popcll(__ballot(n > 0));
+    }
+    int64_t tot = wave_total(part);
+    int eff = c0;
     int64_t P;
     if (fixed_P > 0) {
         P = fixed_P;
     } else {
-        P = (tot + nwg - 1) / nwg;
-        P = ((P + kTile - 1) / kTile) * kTile;
-        if (P < kTile)
-            P = kTile;
+        P = slice_positions((uint32_t)tot, (uint32_t)nwg);
+        if (startup < 0) {
+            const int64_t charged = tot + (int64_t)(-startup) * nnz;
+            if (slice_positions((uint32_t)charged, (uint32_t)nwg) == P) {
+                tot = charged;
+                eff = -startup;
+            }
+        }
     }
-    return {tot, P};
+    return {tot, P, eff};
 }
 
 // Lanes (sequences of a 64-sequence chunk starting at flat position `pre`,
@@ -548,7 +575,7 @@ decode_split_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const 
                 sp = seq_span(seqlens[b0 + lane], Tmax, APPEND, window);
         }
         const int Lc = sp.n;
-        const int incl = wave_incl_scan(with_startup(Lc, startup));
+        const int incl = wave_incl_scan(with_startup(Lc, pt.startup));
         const int64_t chunk_total = __builtin_amdgcn_readlane(incl, 63);
         if (pre + chunk_total <= lo) {
             pre += chunk_total;
@@ -768,7 +795,7 @@ decode_wide_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const _
                 sp = seq_span(seqlens[b0 + lane], Tmax, APPEND, window);
         }
         const int Lc = sp.n;
-        const int incl = wave_incl_scan(with_startup(Lc, startup));
+        const int incl = wave_incl_scan(with_startup(Lc, pt.startup));
         const int64_t chunk_total = __builtin_amdgcn_readlane(incl, 63);
         if (pre + chunk_total <= lo) {
             pre += chunk_total;
@@ -1037,29 +1064,40 @@ decode_merge_kernel(const int32_t *__restrict__ seqlens, int B, int H, int Tmax,
 
     // partition and this sequence's first real flat position, after its
     // startup positions (each wave on its own)
-    int tot_part = 0, pre_part = 0, L_first = 0;
-    for (int i = lane; i < B; i += 64) {
-        const int Li = seq_span(seqlens[i], Tmax, append, window).n;
-        tot_part += with_startup(Li, startup);
+    const int c0 = startup < 0 ? 0 : startup;
+    int tot_part = 0, pre_part = 0, L_first = 0, nnz = 0, pre_nnz = 0;  // counts wave-uniform
+    for (int i0 = 0; i0 < B; i0 += 64) {
+        const int i = i0 + lane;
+        const int Li = i < B ? seq_span(seqlens[i], Tmax, append, window).n : 0;
+        tot_part += with_startup(Li, c0);
+        nnz += __popcll(__ballot(Li > 0));
+        pre_nnz += __popcll(__ballot(Li > 0 && i < b));
         if (i < b)
-            pre_part += with_startup(Li, startup);
-        if (i == lane)
+            pre_part += with_startup(Li, c0);
+        if (i0 == 0)
             L_first = Li;
     }
     // 32-bit arithmetic: flat positions stay below 2^31 (the host checks
     // B * (Tmax + startup) < 2^31), and the slice length is the same as the
     // decode kernels' (make_partition).
-    const uint32_t tot = (uint32_t)wave_total(tot_part);
-    const uint32_t pre_b = (uint32_t)wave_total(pre_part) + (uint32_t)startup;
+    uint32_t tot = (uint32_t)wave_total(tot_part);
+    uint32_t pre0 = (uint32_t)wave_total(pre_part);
+    int eff = c0;
     uint32_t P;
     if (fixed_P > 0) {
         P = (uint32_t)fixed_P;
     } else {
-        P = (tot + (uint32_t)nwg - 1) / (uint32_t)nwg;
-        P = ((P + kTile - 1) / kTile) * kTile;
-        if (P < (uint32_t)kTile)
-            P = kTile;
+        P = slice_positions(tot, (uint32_t)nwg);
+        if (startup < 0) {
+            const uint32_t charged = tot + (uint32_t)(-startup) * (uint32_t)nnz;
+            if (slice_positions(charged, (uint32_t)nwg) == P) {
+                tot = charged;
+                eff = -startup;
+                pre0 += (uint32_t)eff * (uint32_t)pre_nnz;
+            }
+        }
     }
+    const uint32_t pre_b = pre0 + (uint32_t)eff;
 
     const int h = item / NDC, dc = item % NDC;
     const int sl = lane / NQ, qd = lane % NQ;

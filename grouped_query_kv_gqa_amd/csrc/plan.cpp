@@ -183,19 +183,25 @@ gqa_status plan_decode(int B, int H, int G, int d_h, int Tmax, gqa_dtype dtype, 
     const int64_t combos = (int64_t)(G / p.gb) * p.head_tiles;
     if (combos > 65535)
         return fail(err, GQA_ERR_UNSUPPORTED, "too many key/value heads");
-    // Startup positions (wide kernel only): the piece startup cost over the
+    // Startup positions for the wide kernel: the piece startup cost over the
     // bytes a workgroup streams per position (one group's K and V rows). The
     // narrow kernel reads 8 groups per position, where a piece's start costs
-    // a few positions only, and there the charge measured slower: it moves
-    // slice boundaries off sequence boundaries in uniform batches, giving
-    // workgroups two pieces each.
+    // about one tile; a fixed charge there measured slower, since in uniform
+    // batches it moves slice boundaries off sequence boundaries (giving
+    // workgroups two pieces each) and can raise the tile-rounded slice
+    // length, so the narrow kernel's charge below is conditional.
     if (split_tokens == 0 && p.wide) {
         const int64_t per_pos = (int64_t)p.gb * d_h * 2 * elem_size(dtype);
         p.startup = (int)std::min<int64_t>(kPieceStartupBytes / per_pos, 4096);
         if ((int64_t)B * (Tmax + p.startup) > 0x7fffffff)
             p.startup = 0;  // keep flat positions within 31 bits
     }
-    const int64_t positions = (int64_t)B * (Tmax + p.startup);
+    // Narrow kernel: a one-tile charge per sequence, which the kernels apply
+    // only when it leaves the tile-rounded slice length unchanged (negative:
+    // decided on the device from the lengths).
+    if (split_tokens == 0 && !p.wide && (int64_t)B * (Tmax + kDecodeTile) <= 0x7fffffff)
+        p.startup = -kDecodeTile;
+    const int64_t positions = (int64_t)B * (Tmax + std::max(p.startup, 0));
     const int64_t max_pieces = ceil_div(positions > 0 ? positions : 1, kDecodeTile);
     int64_t nwg;
     if (split_tokens > 0) {

@@ -24,7 +24,8 @@ struct DecodePlan {
     int nwg = 1;         // workgroups along the flat position space (grid x)
     int fixed_P = 0;     // piece length when set by the caller, else 0 (balanced on the device)
     int full_P = 32;     // piece length when every sequence has Tmax positions
-    int startup = 0;     // virtual positions before each sequence (the cost of starting a piece); 0 with fixed_P
+    int startup = 0;     // virtual positions before each sequence (the cost of starting a piece); 0 with
+                         // fixed_P; negative: that many, where the kernels find it leaves P unchanged
     int merge_nq = 8;    // merge kernel: d-quads per wave (64/merge_nq lanes share a quad)
     int merge_u = 4;     // merge kernel: pieces each slot lane loads per round (4 or 16)
     int64_t part_offset = 0;      // fp32 partial rows [nwg + B][H][d_h]
