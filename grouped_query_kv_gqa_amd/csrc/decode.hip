@@ -69,6 +69,18 @@ struct TileCfg {
     static constexpr int HEADS = 16 * NT;
 };
 
+template <int D>
+struct RowSwz {
+    // LDS row swizzles: 16-byte chunk c of tile row r sits at slot c ^ f(r).
+    // K: the 16 rows a score fragment read takes at one chunk go to 16
+    // different slots (d_h = 128: 16 chunks per row; d_h = 64: 8 chunks, rows
+    // of one parity share a bank half).
+    static __device__ __forceinline__ int k(int r) { return D >= 128 ? (r & 15) : ((r >> 1) & 7); }
+    // V: chunk pairs move together (a transposing read takes 8 bytes of a
+    // 32-byte pair); the 8 rows of a half-wave's read go to 8 different pairs.
+    static __device__ __forceinline__ int v(int r) { return D >= 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
+};
+
 __device__ __forceinline__ u32x4_t load16(const __bf16 *p)
 {
     return *reinterpret_cast<const u32x4_t *>(p);
@@ -301,12 +313,12 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
         const int tn = tc + stride;  // the tile these buffers take next
 
         // K tile into this wave's LDS rows, 16-byte chunk c of row r at slot
-        // c ^ (r mod CH), then the next K into the freed registers.
+        // c ^ RowSwz::k(r), then the next K into the freed registers.
 #pragma unroll
         for (int i = 0; i < C::VLOADS; ++i) {
             const int tl = i * C::VROWS + lane / C::CH;
             const int c = lane % C::CH;
-            *reinterpret_cast<u32x4_t *>(kl + tl * D + ((c ^ (tl % C::CH)) * 8)) = kbf[i];
+            *reinterpret_cast<u32x4_t *>(kl + tl * D + ((c ^ RowSwz<D>::k(tl)) * 8)) = kbf[i];
         }
         compiler_fence();
         __builtin_amdgcn_sched_barrier(0);
@@ -322,7 +334,7 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
 #pragma unroll
             for (int s = 0; s < C::KS; ++s) {
                 const int row = mt * 16 + col, ch = s * 4 + kb;
-                kf[s] = *reinterpret_cast<const bf16x8_t *>(kl + row * D + ((ch ^ (row % C::CH)) * 8));
+                kf[s] = *reinterpret_cast<const bf16x8_t *>(kl + row * D + ((ch ^ RowSwz<D>::k(row)) * 8));
             }
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
@@ -416,7 +428,8 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
     if (any_tile) {
         for (;;) {
             if (prio) {
-                const int level = __builtin_amdgcn_readfirstlane((slice_done + t0 - ta) * 4 / slice_len);
+                const int level =
+                    __builtin_amdgcn_readfirstlane((int)((int64_t)(slice_done + t0 - ta) * 4 / slice_len));
                 if (level <= 0)
                     __builtin_amdgcn_s_setprio(3);
                 else if (level == 1)
@@ -644,16 +657,6 @@ decode_split_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const 
 //    or one partial row per head.
 
 // LDS chunk swizzles of a stage row r (16-byte chunk c sits at slot c ^ f(r)).
-template <int D>
-struct WideSwz {
-    // K: the 16 rows a score fragment read takes at one chunk go to 16
-    // different slots (d_h = 128: 16 chunks per row; d_h = 64: 8 chunks, rows
-    // of one parity share a bank half).
-    static __device__ __forceinline__ int k(int r) { return D >= 128 ? (r & 15) : ((r >> 1) & 7); }
-    // V: chunk pairs move together (a transposing read takes 8 bytes of a
-    // 32-byte pair); the 8 rows of a half-wave's read go to 8 different pairs.
-    static __device__ __forceinline__ int v(int r) { return D >= 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
-};
 
 constexpr int kWideWaves = 8;
 constexpr int kWideHeadTiles = 4;                         // 16-head tiles per workgroup
@@ -696,7 +699,7 @@ decode_wide_kernel(const __bf16 *__restrict__ q, __bf16 *kc, __bf16 *vc, const _
     constexpr int NI = kWideRows / (RPI * kWideWaves);  // load instructions per wave per tensor
     static_assert(NI >= 1 && kWideRows % (RPI * kWideWaves) == 0, "stage rows split evenly over the waves");
     constexpr int TILE = kWideRows * D;  // elements of one stage tensor
-    using SW = WideSwz<D>;
+    using SW = RowSwz<D>;
     // Separate arrays: the compiler then knows the loads into one buffer do
     // not touch the buffer being read.
     __shared__ __attribute__((aligned(256))) __bf16 K0[TILE];
