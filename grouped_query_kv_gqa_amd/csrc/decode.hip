@@ -424,17 +424,22 @@ __device__ __forceinline__ void decode_piece(const __bf16 *__restrict__ q, __bf1
     // 196.9 -> 193.5 us per call. Slices under kPrioMinPositions keep one
     // priority: on the Llama-3-8B layer (256 positions per slice) the
     // scheme measured 1% slower.
+    // (Quarter marks of the slice, relative to this piece's tiles: compares
+    // only inside the loop.)
     const bool prio = slice_len >= kPrioMinPositions;
+    auto mark = [&](int num) {  // position of the slice's num/4 mark in this piece (clamped to int)
+        return (int)min<int64_t>((int64_t)ta - slice_done + (int64_t)slice_len * num / 4, INT32_MAX);
+    };
+    const int q1 = mark(1), q2 = mark(2), q3 = mark(3);
     if (any_tile) {
         for (;;) {
             if (prio) {
-                const int level =
-                    __builtin_amdgcn_readfirstlane((int)((int64_t)(slice_done + t0 - ta) * 4 / slice_len));
-                if (level <= 0)
+                const int t = __builtin_amdgcn_readfirstlane(t0);
+                if (t < q1)
                     __builtin_amdgcn_s_setprio(3);
-                else if (level == 1)
+                else if (t < q2)
                     __builtin_amdgcn_s_setprio(2);
-                else if (level == 2)
+                else if (t < q3)
                     __builtin_amdgcn_s_setprio(1);
                 else
                     __builtin_amdgcn_s_setprio(0);
