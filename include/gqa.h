@@ -86,7 +86,11 @@ typedef enum gqa_dtype { GQA_BF16 = 0, GQA_FP32 = 1, GQA_FP16 = 2 } gqa_dtype;
  * (hipMallocAsync on `stream`) by the first 16-bit call that needs it and
  * replaced by a larger one when a later call needs more. Calls on one stream
  * are ordered by that stream; calls on different streams use different
- * blocks. gqa_release_workspaces() frees them all.
+ * blocks. gqa_release_workspaces() frees them all. Blocks are keyed by the
+ * stream handle: a destroyed stream's block stays allocated, and a stream
+ * created later with the same handle takes it over, so call
+ * gqa_release_workspaces() after destroying streams whose work may still be
+ * running.
  *
  * Graph capture. A call made while `stream` is being captured never
  * allocates: if the stream's workspace is missing or too small it returns
