@@ -18,6 +18,9 @@ windows, fp16, weighted pooling). "copy_ceiling" measures plain streaming
 read and copy kernels over 1 GiB as the practical bandwidth ceiling next to
 the 8 TB/s peak, and each decode workload's roofline carries "plain_read",
 the same plain read over that workload's bytes and input rotation.
+"gemm_ceiling" is its matrix-core counterpart: a plain library bf16 GEMM
+(torch.matmul, 8192^3) timed like the prefill, whose rate the prefill
+roofline's "of_gemm_ceiling" compares against.
 
 Inputs are synthetic (seeded N(0,1), no datasets or weights) and resident in
 HBM before timing starts. A workload whose cache is below 1 GiB rotates
@@ -348,6 +351,36 @@ def copy_ceiling(args):
     return res
 
 
+def gemm_ceiling(args):
+    """Practical matrix-core ceiling, the counterpart of the copy ceiling: a
+    plain library GEMM (torch.matmul on bf16, served by hipBLASLt), C = A B
+    with M = N = K = 8192 (1.1 TFLOP per call), both operands contiguous.
+    Timed like the prefill: warmup, the settle period (the clock falls under
+    sustained matrix-core load), then event-timed calls. A reference for
+    what the chip sustains on a dense bf16 contraction, not a bound."""
+    import torch
+
+    n = 8192
+    g = torch.Generator(device="cuda").manual_seed(args.seed + 7)
+    a = torch.randn(n, n, device="cuda", dtype=torch.float32, generator=g).to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.float32, generator=g).to(torch.bfloat16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+
+    def step(i):
+        torch.matmul(a, b, out=c)
+
+    steps = 20
+    _, mean_ms, per, settle = timed_calls(step, steps, 3, args.settle_ms, torch.cuda.current_stream(), every=2)
+    flops = 2 * n ** 3
+    tf = flops / (mean_ms * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"kernel": "torch.matmul bf16 (hipBLASLt), M = N = K = 8192, contiguous operands",
+            "flops_per_call": flops, "steps": steps, "settle_calls": settle, "ms_per_call": round(mean_ms, 4),
+            "TFLOPs": round(tf, 1), "peak_TFLOPs": BF16_MFMA_PEAK_TFLOPS,
+            "frac_of_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
+
+
 def _time_calls(fn, steps, warmup, settle_ms=0.0):
     """Mean milliseconds per call: HIP events on the current stream around
     `steps` back-to-back calls after `warmup` untimed ones and a settle."""
@@ -630,6 +663,10 @@ def main():
         pentry, px = run_prefill(args)
         line["prefill"] = pentry
         pf = (pentry, px)
+        if not args.no_ceiling:
+            gc = gemm_ceiling(args)
+            line["gemm_ceiling"] = gc
+            pentry["roofline"]["of_gemm_ceiling"] = round(pentry["roofline"]["achieved"] / gc["TFLOPs"], 4)
     if not args.no_next:
         line["next"] = run_next(args)
     if not args.no_cpu_baseline:
