@@ -408,6 +408,49 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         ps = add_pair<E>(x, ps);
     };
 
+    // Step in which word w of P_j starts (its FMAs); its pack lands two steps
+    // later, before the P V step that reads its word group.
+    constexpr auto p_slot = [](int w) {
+        if constexpr (D == 128)
+            return w < 4 ? w / 2 : w - 2;
+        else
+            return w / 2;
+    };
+    static_assert([p_slot] {
+        for (int w = 0; w < 16; ++w)
+            if (!(p_slot(w) + 2 < C::KS + C::DT * (w / 4)))
+                return false;
+        return true;
+    }(), "every word is packed before the P V step that reads it");
+    // The same words in three stages spread over consecutive steps of the
+    // pipelined iteration: the two FMAs of word w in step p_slot(w), its two
+    // exponentials in the next step and its pack and row-sum add in the one
+    // after (steps 0..KS-1 are the QK steps, KS + s the P V steps). No
+    // instruction then waits on a result issued just before it, which in
+    // this in-order wave would also hold back the next MFMA. Scores are
+    // turned into probabilities in place.
+    auto p_stage = [&](f32x16_t (&s)[2], int slot, u32x4_t (&pw)[4]) {
+#pragma unroll
+        for (int w = 0; w < 16; ++w)
+            if (p_slot(w) + 2 == slot)
+                pw[w >> 2][w & 3] = pack2<E>(s[w >> 3][8 * ((w >> 2) & 1) + 2 * (w & 3)],
+                                             s[w >> 3][8 * ((w >> 2) & 1) + 2 * (w & 3) + 1]);
+#pragma unroll
+        for (int w = 0; w < 16; ++w)
+            if (p_slot(w) + 1 == slot) {
+                const int v0 = 8 * ((w >> 2) & 1) + 2 * (w & 3);
+                s[w >> 3][v0] = fast_exp2(s[w >> 3][v0]);
+                s[w >> 3][v0 + 1] = fast_exp2(s[w >> 3][v0 + 1]);
+            }
+#pragma unroll
+        for (int w = 0; w < 16; ++w)
+            if (p_slot(w) == slot) {
+                const int v0 = 8 * ((w >> 2) & 1) + 2 * (w & 3);
+                s[w >> 3][v0] = fmaf(s[w >> 3][v0], scale_log2, -m_run);
+                s[w >> 3][v0 + 1] = fmaf(s[w >> 3][v0 + 1], scale_log2, -m_run);
+            }
+    };
+
     f32x16_t acc[C::DT];
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
@@ -432,20 +475,10 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     // left) the reference update.
     constexpr int kPfDist = 2;  // LDS fragment reads run this many steps ahead
     constexpr int kPvSteps = 4 * C::DT;
-    // P_j words: the first kQkWords during the QK steps, the rest during the
-    // first P V steps, each before the step whose MFMA reads it; then the
-    // row max of S_{j+1} (8 steps), late enough for the last QK MFMAs.
-    constexpr bool kSplitP = D == 128;
-    constexpr int kQkWords = kSplitP ? 10 : 16;
-    constexpr auto qk_w0 = [](int ks) {  // first word computed in QK step ks
-        if constexpr (kSplitP)
-            return ks < 2 ? 2 * ks : ks + 2;
-        else
-            return ks * (16 / C::KS);
-    };
-    static_assert(qk_w0(C::KS) == kQkWords, "QK steps cover their words");
-    static_assert(16 - kQkWords <= 8 * C::DT, "late words precede their P V step");
-    constexpr int kMaxStart = kSplitP ? 16 - kQkWords : (kPvSteps >= 12 ? 4 : 0);
+    // P_j words go through p_stage in every step; the row max of S_{j+1}
+    // takes 8 P V steps from kMaxStart, late enough for the last QK MFMAs
+    // (d_h = 128: after the P V steps that still carry most of P_j's words).
+    constexpr int kMaxStart = D == 128 ? 6 : (kPvSteps >= 12 ? 4 : 0);
     static_assert(kMaxStart + 8 <= kPvSteps, "row max takes 8 steps");
     constexpr bool kEarlyFinish = kMaxStart + 8 < kPvSteps;  // a P V step is left after the maximum
     auto iter = [&](auto P, int j) {
@@ -461,7 +494,6 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
         f32x16_t(&sc)[2] = st[p];
         f32x16_t(&sn)[2] = st[1 - p];
         u32x4_t pw[4];
-        float ps0 = 0.f, ps1 = 0.f;
         __builtin_amdgcn_sched_barrier(0);
 
         // Fragments are read kPfDist steps ahead of their MFMA; inside a step
@@ -487,9 +519,7 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
             }
             sn[0] = mfma32x32x16<E>(kf[ks][0], qf[ks], sn[0]);
             sn[1] = mfma32x32x16<E>(kf[ks][1], qf[ks], sn[1]);
-#pragma unroll
-            for (int w = qk_w0(ks); w < qk_w0(ks + 1); ++w)
-                p_word(sc, w, pw, ps0, ps1);
+            p_stage(sc, ks, pw);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
             __builtin_amdgcn_sched_group_barrier(0x402, 32 / C::KS, 0);  // VALU incl. transcendental
@@ -512,8 +542,7 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
             if (s + kPfDist < kPvSteps)
                 vf[s + kPfDist] = vfrag(Vc, (s + kPfDist) / C::DT, (s + kPfDist) % C::DT);
             acc[dt] = mfma32x32x16<E>(vf[s], __builtin_bit_cast(bf16x8_t, pw[kstep]), acc[dt]);
-            if (s < 16 - kQkWords)
-                p_word(sc, kQkWords + s, pw, ps0, ps1);
+            p_stage(sc, C::KS + s, pw);
             if (s >= kMaxStart && s < kMaxStart + 8)
                 max_part(sn, 2 * (s - kMaxStart), mx0, mx1);
             if (kEarlyFinish && s == kMaxStart + 8) {
@@ -528,6 +557,14 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
             __builtin_amdgcn_sched_barrier(0);
+        }
+        // Row sums after the last P V step: inside the MFMA steps these 16
+        // adds cost more issue time than here (measured 6% slower per call).
+        float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+            float &ps = (w & 1) ? ps1 : ps0;
+            ps = add_pair<E>(pw[w >> 2][w & 3], ps);
         }
         l_run += ps0 + ps1;
         if constexpr (!kEarlyFinish)
