@@ -25,8 +25,10 @@
 //  * Software pipeline over key tiles: while the matrix cores compute the
 //    scores of tile j+1, the vector ALUs turn the scores of tile j into
 //    probabilities; while they compute P_j V_j, the ALUs take the row maxima
-//    of tile j+1. K runs one tile ahead of V, so each load has a whole
-//    iteration to land.
+//    of tile j+1. Each pair of probabilities goes through its FMA, its
+//    exponential and its pack in three consecutive steps, so no vector
+//    instruction waits on the one just before it. K runs one tile ahead of
+//    V, so each load has a whole iteration to land.
 //  * Causal: a query tile only visits key tiles up to its last token; the
 //    heaviest tiles are launched first. Workgroups are numbered so that each
 //    XCD (workgroup i runs on XCD i % 8) takes a contiguous run of query
@@ -395,7 +397,7 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     };
 
     // The row sum adds the bf16-rounded p that the P V product uses (dot
-    // product with (1, 1)).
+    // product with (1, 1)). One word in one go, for the plain iterations.
     // Word w (0..15) of P_j: the bf16 pair for scores st[mt][8*qh + 2*i],
     // +1 (kk = w/4 = 2*mt + qh, i = w%4), word i of pw[kk].
     auto p_word = [&](const f32x16_t (&st)[2], int w, u32x4_t (&pw)[4], float &ps0, float &ps1) {
@@ -471,8 +473,9 @@ prefill_mfma_kernel(const __bf16 *__restrict__ q, const __bf16 *kp, const __bf16
     // laid out by hand in steps fenced with sched_barrier: each QK step
     // issues the K reads of the next step, two MFMAs and a chunk of the
     // softmax of S_j; each P V step issues the V^T reads of the next step,
-    // one MFMA and part of the row maximum of S_{j+1}, then (when a step is
-    // left) the reference update.
+    // one MFMA, the last stages of P_j's words and part of the row maximum
+    // of S_{j+1}, then (when a step is left) the reference update; the row
+    // sums of P_j follow the last P V step.
     constexpr int kPfDist = 2;  // LDS fragment reads run this many steps ahead
     constexpr int kPvSteps = 4 * C::DT;
     // P_j words go through p_stage in every step; the row max of S_{j+1}
