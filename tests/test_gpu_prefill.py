@@ -85,6 +85,49 @@ def test_prefill_row_equals_decode():
         assert torch.max(torch.abs(dec.float() - out[:, t].float())).item() <= 8e-3
 
 
+@pytest.mark.parametrize("H,G,D,dtype", [
+    (32, 8, 128, torch.bfloat16),
+    (24, 8, 128, torch.bfloat16),    # 3 heads per group: a 256-row tile holds 85 1/3 tokens
+    (20, 4, 64, torch.bfloat16),     # 5 heads per group
+    (16, 16, 128, torch.bfloat16),   # multi-head
+    (64, 1, 128, torch.bfloat16),    # multi-query, 64 heads
+    (32, 8, 128, torch.float16),
+    (512, 1, 64, torch.bfloat16),    # a group wider than the MFMA tile: row kernel
+])
+def test_prefill_group_tag_exact(H, G, D, dtype):
+    """Group map of the prefill, exactly ("Grouped-Query Attention"
+    (llm-arch-kb), section 2 The grouping): with every value row of group g
+    in sequence b set to the tag g + G*b, each output row is a convex
+    combination of equal rows, so head h of sequence b must come out as
+    exactly h // (H/G) + G*b (the tags are small integers, exact in 16 bits;
+    the kernel's rounding is far below half a unit in their last place)."""
+    say(f"prefill group tag H={H} G={G} d_h={D} {dtype}")
+    B, T = 2, 150
+    w = I.PrefillWorkload("tag", B, T, H, G, D, dtype)
+    x = I.prefill_inputs(w, seed=H + G + D, device=DEV)
+    tag = (torch.arange(G, device=DEV, dtype=torch.float32).view(1, 1, G, 1)
+           + G * torch.arange(B, device=DEV, dtype=torch.float32).view(B, 1, 1, 1))
+    x["v"] = tag.expand(B, T, G, D).to(dtype).contiguous()
+    expect = (torch.arange(H, device=DEV) // (H // G)).view(1, 1, H, 1).float() \
+        + G * torch.arange(B, device=DEV).view(B, 1, 1, 1).float()
+    for causal, window in [(True, 0), (False, 0), (True, 40)]:
+        torch.cuda.synchronize()
+        out = gq.prefill(x["q"], x["k"], x["v"], causal=causal, window=window)
+        torch.cuda.synchronize()
+        assert torch.equal(out.float(), expect.expand(B, T, H, D)), (H, G, D, dtype, causal, window)
+
+
+def test_prefill_deterministic():
+    """Repeated prefill calls on the same inputs are bit-identical (no
+    atomics; every output row is reduced in a fixed order)."""
+    say("prefill determinism")
+    w = I.PrefillWorkload("det", 2, 1000, 32, 8, 128, torch.bfloat16)
+    x = I.prefill_inputs(w, seed=5, device=DEV)
+    a = _run(x, True).clone()
+    b = _run(x, True)
+    assert torch.equal(a, b)
+
+
 def test_prefill_errors():
     say("prefill argument errors")
     q = torch.zeros(1, 4, 6, 128, dtype=torch.bfloat16, device=DEV)
