@@ -101,6 +101,31 @@ def test_decode_append_split_before_new_token(B, H, G, D, Tmax, seqlens, split, 
         _check(ww, xx, kn, vn, 0, split)
 
 
+@pytest.mark.parametrize("H,G", [(32, 8), (64, 1), (96, 2), (24, 4)])
+def test_decode_step_group_tag_exact(H, G):
+    """Group map of the decode step, exactly ("Grouped-Query Attention"
+    (llm-arch-kb), section 2 The grouping): every cached value row of group
+    g in sequence b, and the appended one, carries the tag g + G*b, so head
+    h of sequence b must come out as exactly h // (H/G) + G*b, with and
+    without a window, for full, empty and partly filled caches."""
+    say(f"decode_step group tag H={H} G={G}")
+    B, D, Tmax = 4, 128, 200
+    w, x, kn, vn = _case(B, H, G, D, Tmax, [200, 0, 77, 199], torch.bfloat16, seed=H + G)
+    tag = (torch.arange(G, device=DEV, dtype=torch.float32).view(1, G, 1)
+           + G * torch.arange(B, device=DEV, dtype=torch.float32).view(B, 1, 1))
+    x["v_cache"] = tag.view(B, 1, G, 1).expand(B, Tmax, G, D).to(torch.bfloat16).contiguous()
+    vn = tag.expand(B, G, D).to(torch.bfloat16).contiguous()
+    expect = ((torch.arange(H, device=DEV) // (H // G)).view(1, H, 1).float()
+              + G * torch.arange(B, device=DEV).view(B, 1, 1).float()).expand(B, H, D)
+    for window, split in [(0, 0), (0, 32), (50, 0)]:
+        k, v = x["k_cache"].clone(), x["v_cache"].clone()
+        torch.cuda.synchronize()
+        out = gq.decode_step(x["q"], k, v, x["seqlens"], scale=w.scale, k_new=kn, v_new=vn, window=window,
+                             split_tokens=split)
+        torch.cuda.synchronize()
+        assert torch.equal(out.float(), expect), (H, G, window, split)
+
+
 def test_decode_step_plain_matches_decode():
     w = I.DecodeWorkload("plain", 3, 32, 8, 128, 700, torch.bfloat16)
     say("decode_step without append or window equals gqa_decode")

@@ -91,6 +91,7 @@ def test_prefill_row_equals_decode():
     (20, 4, 64, torch.bfloat16),     # 5 heads per group
     (16, 16, 128, torch.bfloat16),   # multi-head
     (64, 1, 128, torch.bfloat16),    # multi-query, 64 heads
+    (96, 2, 128, torch.bfloat16),    # 48 heads per group: 5 tokens per 256-row tile
     (32, 8, 128, torch.float16),
     (512, 1, 64, torch.bfloat16),    # a group wider than the MFMA tile: row kernel
 ])
