@@ -262,3 +262,16 @@ int main() {
                     "-o", str(exe)], check=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and "ok" in r.stdout, r.stdout + r.stderr
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asked for several (by flag or by a launcher's
+    WORLD_SIZE) it exits with a message before touching any device."""
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for argv, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *argv], capture_output=True, text=True,
+                           timeout=120, env={**os.environ, **env})
+        assert r.returncode == 2, (argv, env, r.returncode, r.stderr)
+        assert "one GPU only" in r.stderr
