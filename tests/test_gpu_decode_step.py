@@ -126,6 +126,35 @@ def test_decode_step_group_tag_exact(H, G):
         assert torch.equal(out.float(), expect), (H, G, window, split)
 
 
+@pytest.mark.parametrize("H,G,dtype", [(32, 8, torch.bfloat16), (64, 1, torch.bfloat16), (24, 4, torch.float16)])
+def test_decode_step_window_one_is_exact(H, G, dtype):
+    """A window of one position leaves each query only the newest key: with
+    an append that is the new token, so out[b, h] must equal
+    v_new[b, h // (H/G)] bit for bit; without one it is the newest cached
+    row (empty sequences give zero rows)."""
+    say(f"decode_step window 1 H={H} G={G} {dtype}")
+    B, D, Tmax = 4, 128, 90
+    seqlens = [90, 0, 37, 89]
+    w, x, kn, vn = _case(B, H, G, D, Tmax, seqlens, dtype, seed=H + 3 * G)
+    r = H // G
+    for split in (0, 32):
+        k, v = x["k_cache"].clone(), x["v_cache"].clone()
+        torch.cuda.synchronize()
+        out = gq.decode_step(x["q"], k, v, x["seqlens"], scale=w.scale, k_new=kn, v_new=vn, window=1,
+                             split_tokens=split)
+        torch.cuda.synchronize()
+        # a full cache takes no append: its newest row is the last cached one
+        newest = torch.stack([v[b, min(L, Tmax - 1)] for b, L in enumerate(seqlens)])
+        assert torch.equal(out, newest.repeat_interleave(r, dim=1)), split
+        k, v = x["k_cache"].clone(), x["v_cache"].clone()
+        out = gq.decode_step(x["q"], k, v, x["seqlens"], scale=w.scale, window=1, split_tokens=split)
+        torch.cuda.synchronize()
+        rows = []
+        for b, L in enumerate(seqlens):
+            rows.append(v[b, L - 1] if L > 0 else torch.zeros_like(v[b, 0]))
+        assert torch.equal(out, torch.stack(rows).repeat_interleave(r, dim=1)), split
+
+
 def test_decode_step_plain_matches_decode():
     w = I.DecodeWorkload("plain", 3, 32, 8, 128, 700, torch.bfloat16)
     say("decode_step without append or window equals gqa_decode")

@@ -118,6 +118,23 @@ def test_prefill_group_tag_exact(H, G, D, dtype):
         assert torch.equal(out.float(), expect.expand(B, T, H, D)), (H, G, D, dtype, causal, window)
 
 
+@pytest.mark.parametrize("H,G,D,dtype", [(32, 8, 128, torch.bfloat16), (64, 1, 128, torch.float16),
+                                         (6, 3, 64, torch.bfloat16), (512, 1, 64, torch.bfloat16)])
+def test_prefill_window_one_is_exact(H, G, D, dtype):
+    """A causal window of one position leaves each query a single key: its
+    weight is exactly 1, so row t of head h must equal v[t, h // (H/G)]
+    bit for bit (the window edge, exactly)."""
+    say(f"prefill window 1 H={H} G={G} d_h={D} {dtype}")
+    B, T = 2, 131
+    w = I.PrefillWorkload("w1", B, T, H, G, D, dtype)
+    x = I.prefill_inputs(w, seed=H * 7 + G, device=DEV)
+    torch.cuda.synchronize()
+    out = gq.prefill(x["q"], x["k"], x["v"], causal=True, window=1)
+    torch.cuda.synchronize()
+    expect = x["v"].repeat_interleave(H // G, dim=2).contiguous()
+    assert torch.equal(out, expect)
+
+
 def test_prefill_deterministic():
     """Repeated prefill calls on the same inputs are bit-identical (no
     atomics; every output row is reduced in a fixed order)."""
