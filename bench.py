@@ -404,20 +404,41 @@ def _mfma_entry(flops, ms, cfg):
                          "flops_per_launch": int(flops)}}
 
 
-def run_next(args):
+NEXT_KEYS = ["decode_append", "decode_window", "decode_fp16", "prefill_window", "prefill_fp16", "weighted_pool"]
+
+
+def run_next(args, only=None):
     """The adjacent rows built after the hot path, each timed on its own
     workload: fused append + decode, sliding-window decode and prefill, fp16
-    storage, weighted group pooling. Every input is resident before timing."""
+    storage, weighted group pooling (all of them, or the one named `only`).
+    Every input is resident before timing."""
     import torch
     import grouped_query_kv_gqa_amd as gq
     from grouped_query_kv_gqa_amd import inputs as I
 
     res = {}
     settle = args.settle_ms / 2
-    # fused cache append + decode: the Llama-3-8B layer, every cache one short
-    # of full, so each call writes position 4095 and attends over 4096
-    w = I.WORKLOADS["decode_llama3_8b"]
     ncopy = 4
+    if only in (None, "decode_append"):
+        res.update(_next_decode_append(args, gq, I, torch, settle, ncopy))
+    if only in (None, "decode_window"):
+        res.update(_next_decode_window(args, gq, I, torch, settle))
+    if only in (None, "decode_fp16"):
+        res.update(_next_decode_fp16(args, gq, I, torch, settle, ncopy))
+    if only in (None, "prefill_window"):
+        res.update(_next_prefill_window(args, gq, I, torch, settle))
+    if only in (None, "prefill_fp16"):
+        res.update(_next_prefill_fp16(args, gq, I, torch, settle))
+    if only in (None, "weighted_pool"):
+        res.update(_next_weighted_pool(args, gq, I, torch, settle, ncopy))
+    return res
+
+
+def _next_decode_append(args, gq, I, torch, settle, ncopy):
+    """Fused cache append + decode: the Llama-3-8B layer, every cache one
+    short of full, so each call writes position 4095 and attends over 4096."""
+    res = {}
+    w = I.WORKLOADS["decode_llama3_8b"]
     xs = [I.decode_inputs(w, seed=args.seed + c, device="cuda", seqlens=[w.Tmax - 1] * w.B) for c in range(ncopy)]
     kn = I.random_tensor((w.B, w.G, w.D), seed=args.seed + 50, dtype=w.dtype, device="cuda")
     vn = I.random_tensor((w.B, w.G, w.D), seed=args.seed + 51, dtype=w.dtype, device="cuda")
@@ -435,9 +456,13 @@ def run_next(args):
         "workload": "decode_llama3_8b, caches at 4095 of 4096, append + attend over 4096", "B": w.B, "H": w.H,
         "G": w.G, "d_h": w.D, "dtype": "bf16", "input_copies": ncopy})
     del xs, outs
+    return res
 
-    # sliding-window decode: the ragged Llama-2-70B batch (B=64, lengths
-    # 1024..8192) with a 4096-position window (0.88 GB read: not rotated)
+
+def _next_decode_window(args, gq, I, torch, settle):
+    """Sliding-window decode: the ragged Llama-2-70B batch (B=64, lengths
+    1024..8192) with a 4096-position window (0.88 GB read: not rotated)."""
+    res = {}
     w = I.WORKLOADS["decode_llama2_70b_ragged"]
     W = 4096
     x = I.decode_inputs(w, seed=args.seed, device="cuda")
@@ -450,8 +475,12 @@ def run_next(args):
         "workload": "decode_llama2_70b_ragged with a 4096-position window", "B": w.B, "H": w.H, "G": w.G,
         "d_h": w.D, "context": w.Tmax, "window": W, "dtype": "bf16"})
     del x
+    return res
 
-    # fp16 decode on the Llama-3-8B layer
+
+def _next_decode_fp16(args, gq, I, torch, settle, ncopy):
+    """fp16 decode on the Llama-3-8B layer."""
+    res = {}
     base = I.WORKLOADS["decode_llama3_8b"]
     w = I.DecodeWorkload(base.name + "_fp16", base.B, base.H, base.G, base.D, base.Tmax, torch.float16)
     xs = [I.decode_inputs(w, seed=args.seed + c, device="cuda") for c in range(ncopy)]
@@ -465,8 +494,12 @@ def run_next(args):
         "workload": "decode_llama3_8b with fp16 storage", "B": w.B, "H": w.H, "G": w.G, "d_h": w.D,
         "context": w.Tmax, "dtype": "fp16", "input_copies": ncopy})
     del xs, outs
+    return res
 
-    # prefill: sliding window 4096 (bf16) and plain causal with fp16 storage
+
+def _next_prefill_window(args, gq, I, torch, settle):
+    """Causal prefill with a 4096-position sliding window (bf16)."""
+    res = {}
     pw = I.PREFILL_WORKLOADS[PREFILL_WORKLOAD]
     x = I.prefill_inputs(pw, seed=args.seed, device="cuda")
     out = torch.empty_like(x["q"])
@@ -479,6 +512,13 @@ def run_next(args):
         "G": pw.G, "d_h": pw.D, "window": W, "dtype": "bf16",
         "flops": "4*B*H*d_h*sum_t min(t+1, window)"})
     del x, out
+    return res
+
+
+def _next_prefill_fp16(args, gq, I, torch, settle):
+    """Plain causal prefill with fp16 storage."""
+    res = {}
+    pw = I.PREFILL_WORKLOADS[PREFILL_WORKLOAD]
     w16 = I.PrefillWorkload(pw.name + "_fp16", pw.B, pw.T, pw.H, pw.G, pw.D, torch.float16, True)
     x = I.prefill_inputs(w16, seed=args.seed, device="cuda")
     out = torch.empty_like(x["q"])
@@ -488,9 +528,14 @@ def run_next(args):
         "workload": "prefill_llama3_8b_causal with fp16 storage", "B": pw.B, "T": pw.T, "H": pw.H, "G": pw.G,
         "d_h": pw.D, "dtype": "fp16", "peak": "fp16 dense MFMA peak equals bf16"})
     del x, out
+    return res
 
-    # weighted group pooling of a Llama-2-70B key projection viewed as [d, H, d_h];
-    # 4 input copies (537 MB) rotate so that no call reads its input from the MALL
+
+def _next_weighted_pool(args, gq, I, torch, settle, ncopy):
+    """Weighted group pooling of a Llama-2-70B key projection viewed as
+    [d, H, d_h]; 4 input copies (537 MB) rotate so that no call reads its
+    input from the MALL."""
+    res = {}
     N, H, G, D = 8192, 64, 8, 128
     xins = [I.mean_pool_inputs(N, H, D, dtype=torch.bfloat16, seed=args.seed + c, device="cuda")
             for c in range(ncopy)]
@@ -576,7 +621,8 @@ def main():
     ap.add_argument("--prefill-warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--only", default=None,
-                    help="run one workload only (a decode key, or 'prefill'), e.g. under a profiler")
+                    help="run one workload only (a decode key, 'prefill', or next:<key> for an adjacent "
+                         "row), e.g. under a profiler")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds for the headline CPU baseline")
     ap.add_argument("--cpu-budget-other", type=float, default=2.0, help="seconds per other CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -613,8 +659,10 @@ def main():
         elif args.only in keys:
             key, name, G = next(c for c in DECODE_CONFIGS if c[0] == args.only)
             entry, _, _ = run_decode(key, decode_workload(name, G), args, args.steps, args.warmup)
+        elif args.only.startswith("next:") and args.only[5:] in NEXT_KEYS:
+            entry = run_next(args, only=args.only[5:])[args.only[5:]]
         else:
-            sys.exit(f"--only: one of {sorted(keys) + ['prefill']}")
+            sys.exit(f"--only: one of {sorted(keys) + ['prefill'] + ['next:' + k for k in NEXT_KEYS]}")
         print(json.dumps({"only": args.only, **entry}), flush=True)
         return
 
