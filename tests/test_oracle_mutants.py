@@ -46,6 +46,14 @@ MUTANTS = [
     ("max_of_first_key_only", "if (s[t] > m)\n            m = s[t];", "if (t == 0)\n            m = s[t];"),
     ("pool_strided_groups", "if (oracle_group_of_head(i, H, G) != g)\n                    continue;\n                ++members;",
      "if (i % G != g)\n                    continue;\n                ++members;"),
+    ("values_from_keys", "acc += s[t] * widen(v, key_base", "acc += s[t] * widen(k, key_base"),
+    ("decode_query_of_group", "attend_row(q, row * D, k, v, key_base, key_stride, L, D,",
+     "attend_row(q, ((int64_t)b * H + g) * D, k, v, key_base, key_stride, L, D,"),
+    ("prefill_window_one_short", "int lo = (window > 0 && t + 1 > window) ? t + 1 - window : 0;",
+     "int lo = (window > 0 && t + 1 > window) ? t + 2 - window : 0;"),
+    ("weighted_pool_group_weight", "o[d] += w[i] * widen(in,", "o[d] += w[g] * widen(in,"),
+    ("f16_sign_dropped", "return sign ? -mag : mag;", "return mag;"),
+    ("empty_row_not_zero", "if (L <= 0) {", "if (L < 0) {"),
 ]
 
 
