@@ -54,6 +54,11 @@ MUTANTS = [
     ("weighted_pool_group_weight", "o[d] += w[i] * widen(in,", "o[d] += w[g] * widen(in,"),
     ("f16_sign_dropped", "return sign ? -mag : mag;", "return mag;"),
     ("empty_row_not_zero", "if (L <= 0) {", "if (L < 0) {"),
+    ("prefill_query_of_group",
+     "int64_t q_off = (((int64_t)b * T + t) * H + h) * D;\n        int64_t key_base = ((int64_t)b * T * G + g) * D;",
+     "int64_t q_off = (((int64_t)b * T + t) * H + g) * D;\n        int64_t key_base = ((int64_t)b * T * G + g) * D;"),
+    ("prefill_keys_of_first_sequence", "int64_t key_base = ((int64_t)b * T * G + g) * D;",
+     "int64_t key_base = ((int64_t)g) * D;"),
 ]
 
 
