@@ -1246,21 +1246,24 @@ decode_f32_kernel(const float *__restrict__ q, float *kc, float *vc, const float
         qv[j] = q[row * D + lane + 64 * j];
         acc[j] = 0.f;
     }
-    float m = -INFINITY, l = 0.f;
+    // Scores and the running maximum in fp64, so that the exponent argument
+    // keeps fp32 accuracy at large scores.
+    double m = -INFINITY;
+    float l = 0.f;
     for (int t = 0; t < L; ++t) {
         if (t != t_new && !GQA_IN_RANGE(sp.lo + t, Tmax, 11))
             continue;
         const int64_t off = (((int64_t)b * Tmax + sp.lo + t) * G + g) * D;
         const float *kp = (t == t_new) ? knew + new_off : kc + off;
         const float *vp = (t == t_new) ? vnew + new_off : vc + off;
-        float dot = 0.f;
+        double dot = 0.0;
 #pragma unroll
         for (int j = 0; j < J; ++j)
-            dot += qv[j] * kp[lane + 64 * j];
-        const float s = wave_sum(dot) * scale;
-        const float m_new = fmaxf(m, s);
-        const float alpha = expf(m - m_new);
-        const float p = expf(s - m_new);
+            dot += (double)qv[j] * (double)kp[lane + 64 * j];
+        const double s = wave_sum(dot) * (double)scale;
+        const double m_new = fmax(m, s);
+        const float alpha = expf((float)(m - m_new));
+        const float p = expf((float)(s - m_new));
         l = l * alpha + p;
 #pragma unroll
         for (int j = 0; j < J; ++j)

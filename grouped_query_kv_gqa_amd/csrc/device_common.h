@@ -201,6 +201,14 @@ __device__ __forceinline__ float wave_sum(float x)
     return x;
 }
 
+__device__ __forceinline__ double wave_sum(double x)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        x += __shfl_xor(x, m, 64);
+    return x;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
 // row broadcasts (no LDS round trips): within each row of 16 lanes by shifts
 // of 1, 2, 4 and 8, then row 0's total into row 1, row 2's into row 3, and

@@ -91,7 +91,7 @@ __device__ __forceinline__ void st<_Float16>(_Float16 *p, float x)
 template <typename T, int D>
 __global__ void __launch_bounds__(64)
 prefill_row_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, int T_, int H,
-                   int G, int causal, int window, float scale, T *__restrict__ out)
+                   int G, int causal, int window, double scale, T *__restrict__ out)
 {
     constexpr int J = D / 64;
     const int64_t row = blockIdx.x;  // ((b * T) + t) * H + h
@@ -110,19 +110,23 @@ prefill_row_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
         qv[j] = ld(q + row * D + lane + 64 * j);
         acc[j] = 0.f;
     }
-    float m = -INFINITY, l = 0.f;
+    // Scores and the running maximum in fp64: the exponent argument s - m
+    // then keeps fp32 accuracy however large the scores are (an fp32 score
+    // of magnitude 100 is only good to about 4e-6 in the exponent).
+    double m = -INFINITY;
+    float l = 0.f;
     for (int s = s0; s < nkeys; ++s) {
         if (!GQA_IN_RANGE(s, T_, 3))
             continue;
         const int64_t off = ((b * T_ + s) * G + g) * D;
-        float dot = 0.f;
+        double dot = 0.0;
 #pragma unroll
         for (int j = 0; j < J; ++j)
-            dot += qv[j] * ld(k + off + lane + 64 * j);
-        const float sc = wave_sum(dot) * scale;
-        const float m_new = fmaxf(m, sc);
-        const float alpha = expf(m - m_new);
-        const float p = expf(sc - m_new);
+            dot += (double)qv[j] * (double)ld(k + off + lane + 64 * j);
+        const double sc = wave_sum(dot) * scale;
+        const double m_new = fmax(m, sc);
+        const float alpha = expf((float)(m - m_new));
+        const float p = expf((float)(sc - m_new));
         l = l * alpha + p;
 #pragma unroll
         for (int j = 0; j < J; ++j)
@@ -138,7 +142,7 @@ template <typename T>
 hipError_t launch_rows(const PrefillArgs &a)
 {
     const int64_t rows = (int64_t)a.B * a.T * a.H;
-    const float scale = 1.0f / sqrtf((float)a.D);
+    const double scale = 1.0 / sqrt((double)a.D);
     if (a.D == 64)
         prefill_row_kernel<T, 64><<<dim3((unsigned)rows), 64, 0, a.stream>>>(
             static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v), a.T, a.H, a.G,
