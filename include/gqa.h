@@ -22,7 +22,9 @@
  *     even), GQA_FP16 (the same with IEEE fp16 storage and fp16 MFMA inputs;
  *     the pages' own cache arithmetic counts 2-byte fp16 scalars: "Grouped-Query
  *     Attention" (llm-arch-kb), section 2 Derivation, KV-cache footprint) or
- *     GQA_FP32 (fp32 storage and arithmetic; a debug path).
+ *     GQA_FP32 (fp32 storage, outputs and softmax sums; a debug path whose
+ *     scores and running maxima are kept in fp64, so that its probabilities
+ *     keep fp32 accuracy when scores are large).
  *   - Calls are asynchronous on `stream` (0 = the null stream): they return
  *     once the work is queued. Work on one stream runs in order.
  *   - All argument checks run on the host before anything is queued. A
